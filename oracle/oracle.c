@@ -1,0 +1,235 @@
+/*
+ * oracle.c -- plain, slow CPU reference for the tiled GEMM  C = A * B.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  The HIP library
+ * never links it, includes it or calls it, and this file includes nothing
+ * from the HIP library.
+ *
+ * What is computed.  "Hiding Memory Latency in CUDA: Asynchronous Loads and
+ * Software Pipelines" (introduction) defines the work of a tiled GEMM as
+ * the product of A and B, walked tile by tile along K; "Pipeline GPU Kernel"
+ * (Schritt 5) states that pipelining only reorders the loads and leaves the
+ * arithmetic unchanged.  The result of every pipelined variant is therefore
+ * the plain definition
+ *
+ *        C[i][j] = sum_{k=0}^{K-1} A[i][k] * B[k][j]
+ *
+ * over the already-rounded input values.  This file writes exactly that
+ * definition out: the inputs are decoded exactly to double (float inputs)
+ * or widened to int32 (int8 inputs), and each output is one dot product
+ * accumulated in k order, in double (floats) or int32 (int8).  There is no
+ * blocking, no reordering of the sum and no fused arithmetic beyond that.
+ * OpenMP only splits the independent output rows between threads.
+ *
+ * Layouts (element (r,c) of a matrix):
+ *   A  row-major M x K             A[i*lda + k]
+ *   B  row-major K x N  (b_col=0)  B[k*ldb + j]
+ *   B  col-major K x N  (b_col=1)  B[j*ldb + k]
+ *   C  row-major M x N             C[i*ldc + j]
+ * K = 0 gives C = 0 (the empty sum).  M = 0 or N = 0 writes nothing.
+ *
+ * dtype codes: 0 = binary16, 1 = bfloat16, 3 = binary32 (float inputs,
+ * double output); int8 has its own entry points with int32 output.
+ *
+ * Return codes: 0 ok, -1 invalid argument, -2 int8 K too large for an
+ * exact int32 sum (|a*b| <= 2^14, so K <= 131071 keeps every partial sum
+ * inside int32).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_F16 0
+#define ORACLE_BF16 1
+#define ORACLE_F32 3
+#define ORACLE_I8_MAX_K 131071
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction
+ * bits.  Decoded from the format definition, exactly, into double. */
+double oracle_f16_to_f64(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int e = (h >> 10) & 0x1f;
+    const int f = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24); /* subnormal: f * 2^(1-15-10) */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25); /* (1 + f/2^10) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* bfloat16 is the upper half of an IEEE 754 binary32 word. */
+double oracle_bf16_to_f64(uint16_t b)
+{
+    const uint32_t u = (uint32_t)b << 16;
+    float x;
+    memcpy(&x, &u, sizeof x);
+    return (double)x;
+}
+
+double oracle_f32_to_f64(uint32_t bits)
+{
+    float x;
+    memcpy(&x, &bits, sizeof x);
+    return (double)x;
+}
+
+static double decode(int dtype, const void* base, int64_t idx)
+{
+    switch (dtype) {
+    case ORACLE_F16: return oracle_f16_to_f64(((const uint16_t*)base)[idx]);
+    case ORACLE_BF16: return oracle_bf16_to_f64(((const uint16_t*)base)[idx]);
+    default: return oracle_f32_to_f64(((const uint32_t*)base)[idx]);
+    }
+}
+
+static int set_threads(int nthreads)
+{
+#ifdef _OPENMP
+    return nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+static int check_dims(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                      int b_col, int64_t ldc)
+{
+    if (M < 0 || N < 0 || K < 0) return -1;
+    if (M == 0 || N == 0) return 0; /* nothing is read or written */
+    if (lda < (K > 0 ? K : 1)) return -1;
+    if (b_col ? ldb < (K > 0 ? K : 1) : ldb < (N > 0 ? N : 1)) return -1;
+    if (ldc < (N > 0 ? N : 1)) return -1;
+    return 0;
+}
+
+/* Full product, float inputs, double output. */
+int oracle_gemm_float(int dtype, int64_t M, int64_t N, int64_t K,
+                      const void* A, int64_t lda, const void* B, int64_t ldb,
+                      int b_col, double* C, int64_t ldc, int nthreads)
+{
+    if (dtype != ORACLE_F16 && dtype != ORACLE_BF16 && dtype != ORACLE_F32) return -1;
+    if (check_dims(M, N, K, lda, ldb, b_col, ldc)) return -1;
+    if (M == 0 || N == 0) return 0;
+
+    /* Decode once: a[i][k] row-major, bt[j][k] so every dot product reads
+     * two contiguous rows.  This is a change of layout only. */
+    double* a = (double*)malloc(sizeof(double) * (size_t)(M * (K ? K : 1)));
+    double* bt = (double*)malloc(sizeof(double) * (size_t)(N * (K ? K : 1)));
+    if (!a || !bt) { free(a); free(bt); return -1; }
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t k = 0; k < K; ++k) a[i * K + k] = decode(dtype, A, i * lda + k);
+    for (int64_t j = 0; j < N; ++j)
+        for (int64_t k = 0; k < K; ++k)
+            bt[j * K + k] = decode(dtype, B, b_col ? j * ldb + k : k * ldb + j);
+
+    const int nt = set_threads(nthreads);
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t i = 0; i < M; ++i) {
+        const double* ai = a + i * K;
+        for (int64_t j = 0; j < N; ++j) {
+            const double* bj = bt + j * K;
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k) s += ai[k] * bj[k];
+            C[i * ldc + j] = s;
+        }
+    }
+    free(a);
+    free(bt);
+    return 0;
+}
+
+/* Selected outputs only: out[e] = C[rows[e]][cols[e]], each computed from
+ * the raw inputs as one k-ordered double dot product. */
+int oracle_gemm_float_entries(int dtype, int64_t K, const void* A, int64_t lda,
+                              const void* B, int64_t ldb, int b_col, int64_t n_entries,
+                              const int64_t* rows, const int64_t* cols, double* out,
+                              int nthreads)
+{
+    if (dtype != ORACLE_F16 && dtype != ORACLE_BF16 && dtype != ORACLE_F32) return -1;
+    if (K < 0 || n_entries < 0) return -1;
+    const int nt = set_threads(nthreads);
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t e = 0; e < n_entries; ++e) {
+        const int64_t i = rows[e], j = cols[e];
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            s += decode(dtype, A, i * lda + k) *
+                 decode(dtype, B, b_col ? j * ldb + k : k * ldb + j);
+        out[e] = s;
+    }
+    return 0;
+}
+
+/* Full product, int8 inputs, int32 accumulation and output. */
+int oracle_gemm_int8(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,
+                     const int8_t* B, int64_t ldb, int b_col, int32_t* C, int64_t ldc,
+                     int nthreads)
+{
+    if (check_dims(M, N, K, lda, ldb, b_col, ldc)) return -1;
+    if (K > ORACLE_I8_MAX_K) return -2;
+    if (M == 0 || N == 0) return 0;
+
+    int32_t* a = (int32_t*)malloc(sizeof(int32_t) * (size_t)(M * (K ? K : 1)));
+    int32_t* bt = (int32_t*)malloc(sizeof(int32_t) * (size_t)(N * (K ? K : 1)));
+    if (!a || !bt) { free(a); free(bt); return -1; }
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t k = 0; k < K; ++k) a[i * K + k] = A[i * lda + k];
+    for (int64_t j = 0; j < N; ++j)
+        for (int64_t k = 0; k < K; ++k) bt[j * K + k] = b_col ? B[j * ldb + k] : B[k * ldb + j];
+
+    const int nt = set_threads(nthreads);
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t i = 0; i < M; ++i) {
+        const int32_t* ai = a + i * K;
+        for (int64_t j = 0; j < N; ++j) {
+            const int32_t* bj = bt + j * K;
+            int32_t s = 0;
+            for (int64_t k = 0; k < K; ++k) s += ai[k] * bj[k];
+            C[i * ldc + j] = s;
+        }
+    }
+    free(a);
+    free(bt);
+    return 0;
+}
+
+int oracle_gemm_int8_entries(int64_t K, const int8_t* A, int64_t lda, const int8_t* B,
+                             int64_t ldb, int b_col, int64_t n_entries, const int64_t* rows,
+                             const int64_t* cols, int32_t* out, int nthreads)
+{
+    if (K < 0 || n_entries < 0) return -1;
+    if (K > ORACLE_I8_MAX_K) return -2;
+    const int nt = set_threads(nthreads);
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t e = 0; e < n_entries; ++e) {
+        const int64_t i = rows[e], j = cols[e];
+        int32_t s = 0;
+        for (int64_t k = 0; k < K; ++k)
+            s += (int32_t)A[i * lda + k] * (int32_t)(b_col ? B[j * ldb + k] : B[k * ldb + j]);
+        out[e] = s;
+    }
+    return 0;
+}
+
+/* Exact decode of n stored values (dtype as above) into double. */
+int oracle_decode_array(int dtype, const void* src, int64_t n, double* dst)
+{
+    if (dtype != ORACLE_F16 && dtype != ORACLE_BF16 && dtype != ORACLE_F32) return -1;
+    for (int64_t e = 0; e < n; ++e) dst[e] = decode(dtype, src, e);
+    return 0;
+}
+
+int oracle_max_threads(void)
+{
+    return set_threads(0);
+}
