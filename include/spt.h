@@ -1,0 +1,178 @@
+/*
+ * spt.h -- software-pipelined tiled GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libspt.so.  Plain pointers and sizes only.
+ *
+ * The operation.  "Hiding Memory Latency in CUDA: Asynchronous Loads and
+ * Software Pipelines" (introduction) states the problem: a tiled GEMM in
+ * which each workgroup repeatedly loads a tile of A and B from global
+ * memory, stages it in shared memory (here: LDS), loads fragments into
+ * registers, runs matrix-core multiply-accumulates and advances to the next
+ * K tile.  Every entry point below computes
+ *
+ *        C[i][j] = sum_{k<K} A[i][k] * B[k][j]     (0 <= i < M, 0 <= j < N)
+ *
+ * overwriting C (no alpha/beta scaling).  K = 0 writes zeros.  M = 0 or
+ * N = 0 returns SPT_OK without launching anything.
+ *
+ * Element types.  SPT_F16 (IEEE binary16) and SPT_BF16 (bfloat16) inputs
+ * accumulate in fp32 and write fp32 C; SPT_I8 inputs accumulate in int32
+ * and write int32 C (exact; K <= 131071 so no partial sum can overflow);
+ * SPT_F32 inputs accumulate in fp32 and write fp32 C.
+ *
+ * Layouts.  A is row-major M x K: element (i,k) at A[i*lda + k], lda >= K.
+ * B is row-major K x N (SPT_ROW): element (k,j) at B[k*ldb + j], ldb >= N,
+ * or column-major (SPT_COL): element (k,j) at B[j*ldb + k], ldb >= K.
+ * C is row-major M x N: element (i,j) at C[i*ldc + j], ldc >= N.  Only the
+ * M x N elements of C are written; the rest of each row of C is untouched.
+ *
+ * Alignment.  A, B and C must be 16-byte aligned and every row pitch must be
+ * a whole number of 16-byte units (lda*elt, ldb*elt, ldc*4 divisible by 16),
+ * else SPT_ERR_MISALIGNED.  Operands are read in 16-byte units that never
+ * cross a row's pitch: the library may read A up to M*lda elements, B up to
+ * K*ldb (row-major) or N*ldb (column-major) elements; padding beyond K or N
+ * never enters the result.
+ *
+ * Ownership.  All matrix pointers are DEVICE pointers owned by the caller.
+ * The library never allocates or frees device memory and keeps no pointer
+ * after a call returns.  `stream` is a hipStream_t (NULL = the null
+ * stream); the launch is asynchronous and the call never synchronizes.
+ * The library keeps no mutable global state apart from a thread-local
+ * message for spt_last_error(); concurrent calls from several threads are
+ * safe.
+ *
+ * Errors.  Every entry point returns an int status and never aborts.
+ * Arguments are validated before any HIP call, so invalid calls return
+ * without touching a device.
+ */
+#ifndef SPT_H
+#define SPT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPT_VERSION 10000 /* 1.0.0 = major*10000 + minor*100 + patch */
+
+/* Element type of A and B (C is fp32, or int32 for SPT_I8). */
+enum spt_dtype { SPT_F16 = 0, SPT_BF16 = 1, SPT_I8 = 2, SPT_F32 = 3 };
+
+/* Storage order of B. */
+enum spt_layout { SPT_ROW = 0, SPT_COL = 1 };
+
+/*
+ * Global->LDS producer of the K-loop.
+ *  SYNC    the sequential load-sync-compute-sync loop ("Hiding Memory
+ *          Latency ...", section 1; "Pipeline GPU Kernel", Schritt 1): the
+ *          unpipelined baseline, one LDS stage only.
+ *  REG     register-staged prefetch ("Pipeline GPU Kernel", Schritt 2 and 3,
+ *          the LDG-register variant): tile k+1 is loaded global->VGPR while
+ *          tile k is computed, then written VGPR->LDS between barriers;
+ *          1 LDS stage (register-only prefetch) or 2 (double buffer).
+ *  DIRECT  asynchronous global->LDS copies (the pages' cp.async variant,
+ *          on CDNA4 the buffer_load ... lds instruction, which bypasses the
+ *          VGPRs), in an S-stage LDS ring with S = 2 or 3 ("Hiding Memory
+ *          Latency ...", sections 5 and 6).
+ *  AUTO    the library's choice for the shape.
+ * Valid (variant, stages) pairs: SYNC x 1, REG x {1,2}, DIRECT x {2,3};
+ * stages = 0 picks the variant's default (SYNC 1, REG 2, DIRECT 3).
+ */
+enum spt_variant {
+    SPT_VARIANT_AUTO = 0,
+    SPT_VARIANT_SYNC = 1,
+    SPT_VARIANT_REG = 2,
+    SPT_VARIANT_DIRECT = 3
+};
+
+/*
+ * Workgroup tile menu.  The K depth of a tile is 64 bytes of each row for
+ * SPT_TILE_128x256 (BK = 32 for fp16/bf16, 64 for int8, 16 for fp32) and
+ * 128 bytes for SPT_TILE_256x256.
+ *  SPT_TILE_128x256  128 x 256, 256 threads (2 x 2 waves of 64 x 128): the
+ *                    tile of "Hiding Memory Latency ...", section 6.
+ *  SPT_TILE_256x256  256 x 256, 512 threads (2 x 4 waves of 128 x 64).
+ *  SPT_TILE_128x128  128 x 128, 256 threads (2 x 2 waves of 64 x 64).
+ */
+enum spt_tile {
+    SPT_TILE_AUTO = 0,
+    SPT_TILE_128x256 = 1,
+    SPT_TILE_256x256 = 2,
+    SPT_TILE_128x128 = 3
+};
+
+enum spt_status {
+    SPT_OK = 0,
+    SPT_ERR_INVALID = -1,     /* negative size, null pointer, pitch too small, bad enum */
+    SPT_ERR_UNSUPPORTED = -2, /* (variant, stages, tile, dtype, layout) not built; int8 K > 131071;
+                                 an operand panel too large for 32-bit buffer offsets */
+    SPT_ERR_MISALIGNED = -3,  /* pointer or row pitch not a multiple of 16 bytes */
+    SPT_ERR_LAUNCH = -4       /* the HIP launch reported an error */
+};
+
+/* What a call would launch, and the LDS / occupancy / ratio figures of that
+ * plan ("Pipeline GPU Kernel", Schritt 1 and 2; "Kernel-Engpass
+ * analysieren", Schritt 3 and 6), evaluated for gfx950. */
+typedef struct spt_plan_info {
+    int32_t dtype, b_layout, variant, stages, tile_id;
+    int32_t BM, BN, BK;             /* workgroup tile, K depth in elements */
+    int32_t threads, waves;         /* per workgroup (64-wide waves) */
+    int32_t wave_m, wave_n;         /* per-wave output tile */
+    int32_t elt_bytes;              /* bytes per A/B element */
+    int64_t tiles_m, tiles_n;       /* workgroup tiles along M and N */
+    int64_t grid;                   /* workgroups launched = tiles_m * tiles_n */
+    int64_t k_tiles;                /* ceil(K / BK) */
+    int64_t k_full_tiles;           /* floor(K / BK) */
+    int32_t k_tail;                 /* K mod BK: width of the zero-filled last tile (0 = none) */
+    int32_t a_stage_bytes;          /* BM*BK*elt */
+    int32_t b_stage_bytes;          /* BK*BN*elt */
+    int32_t stage_bytes;            /* a + b */
+    int32_t lds_bytes;              /* stages * stage_bytes (LDS per workgroup) */
+    int32_t a_copies_per_thread;    /* 16-byte accesses per thread per stage */
+    int32_t b_copies_per_thread;
+    int32_t wg_per_cu_lds;          /* floor(163840 / lds_bytes): the LDS limit per CU */
+    int32_t waves_per_simd_lds;     /* wg_per_cu_lds * waves / 4 */
+    int32_t steady_vmcnt;           /* loads that may stay in flight at the steady-state wait */
+    int32_t mfma_per_ktile_per_wave;
+    double ratio_flop_per_byte;     /* 2*BM*BN*BK / ((BM*BK + BK*BN)*elt) */
+    double ratio_mfma_per_load;     /* MFMA instructions per global load instruction, per wave */
+} spt_plan_info;
+
+/* C = A*B with B row-major, the library's choice of tile and variant. */
+int spt_gemm(int64_t M, int64_t N, int64_t K,
+             const void* A, int64_t lda,
+             const void* B, int64_t ldb,
+             void* C, int64_t ldc,
+             int dtype, void* stream);
+
+/* C = A*B with an explicit B layout (spt_layout), producer variant
+ * (spt_variant), LDS stage count (0 = variant default) and tile (spt_tile). */
+int spt_gemm_ex(int64_t M, int64_t N, int64_t K,
+                const void* A, int64_t lda,
+                const void* B, int64_t ldb,
+                void* C, int64_t ldc,
+                int dtype, void* stream,
+                int b_layout, int variant, int stages, int tile_id);
+
+/* Fill *out with the plan spt_gemm_ex would launch for these arguments.
+ * Pure host computation; needs no device.  Same status codes as
+ * spt_gemm_ex for the shape arguments. */
+int spt_plan(int dtype, int64_t M, int64_t N, int64_t K,
+             int b_layout, int variant, int stages, int tile_id,
+             spt_plan_info* out);
+
+/* Static string naming a status code. */
+const char* spt_status_string(int status);
+
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* spt_last_error(void);
+
+/* SPT_VERSION of the loaded library. */
+int spt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPT_H */

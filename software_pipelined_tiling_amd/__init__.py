@@ -1,1 +1,182 @@
-"""software_pipelined_tiling_amd -- software-pipelined tiled GEMM for MI355X (gfx950)."""
+"""software_pipelined_tiling_amd -- software-pipelined tiled GEMM for AMD MI355X (gfx950).
+
+Thin ctypes binding of ``libspt.so`` (C ABI in ``include/spt.h``).  The
+functions ``spt_gemm``, ``spt_gemm_ex``, ``spt_plan``, ``spt_status_string``,
+``spt_last_error`` and ``spt_version`` keep the C names and arguments (device
+pointers as Python ints, ``stream`` as a hipStream_t handle or 0).  ``gemm``
+is a convenience wrapper for torch tensors that only marshals arguments:
+every step of the product runs in the library's HIP kernels, and there is no
+other code path -- if ``libspt.so`` cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "spt_gemm", "spt_gemm_ex", "spt_plan", "spt_status_string", "spt_last_error", "spt_version",
+    "gemm", "plan", "SptError", "PlanInfo", "lib_path",
+    "F16", "BF16", "I8", "F32", "ROW", "COL", "VARIANT_AUTO", "VARIANT_SYNC", "VARIANT_REG",
+    "VARIANT_DIRECT", "TILE_AUTO", "TILE_128x256", "TILE_256x256", "TILE_128x128",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(HERE, "libspt.so")
+
+# enum spt_dtype / spt_layout / spt_variant / spt_tile / spt_status
+F16, BF16, I8, F32 = 0, 1, 2, 3
+ROW, COL = 0, 1
+VARIANT_AUTO, VARIANT_SYNC, VARIANT_REG, VARIANT_DIRECT = 0, 1, 2, 3
+TILE_AUTO, TILE_128x256, TILE_256x256, TILE_128x128 = 0, 1, 2, 3
+SPT_OK, SPT_ERR_INVALID, SPT_ERR_UNSUPPORTED, SPT_ERR_MISALIGNED, SPT_ERR_LAUNCH = 0, -1, -2, -3, -4
+
+DTYPE_CODES = {"f16": F16, "bf16": BF16, "i8": I8, "f32": F32}
+VARIANT_CODES = {"auto": VARIANT_AUTO, "sync": VARIANT_SYNC, "reg": VARIANT_REG, "direct": VARIANT_DIRECT}
+
+
+class PlanInfo(ctypes.Structure):
+    """Mirror of ``spt_plan_info``."""
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("b_layout", ctypes.c_int32), ("variant", ctypes.c_int32),
+        ("stages", ctypes.c_int32), ("tile_id", ctypes.c_int32),
+        ("BM", ctypes.c_int32), ("BN", ctypes.c_int32), ("BK", ctypes.c_int32),
+        ("threads", ctypes.c_int32), ("waves", ctypes.c_int32),
+        ("wave_m", ctypes.c_int32), ("wave_n", ctypes.c_int32), ("elt_bytes", ctypes.c_int32),
+        ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64), ("grid", ctypes.c_int64),
+        ("k_tiles", ctypes.c_int64), ("k_full_tiles", ctypes.c_int64), ("k_tail", ctypes.c_int32),
+        ("a_stage_bytes", ctypes.c_int32), ("b_stage_bytes", ctypes.c_int32),
+        ("stage_bytes", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+        ("a_copies_per_thread", ctypes.c_int32), ("b_copies_per_thread", ctypes.c_int32),
+        ("wg_per_cu_lds", ctypes.c_int32), ("waves_per_simd_lds", ctypes.c_int32),
+        ("steady_vmcnt", ctypes.c_int32), ("mfma_per_ktile_per_wave", ctypes.c_int32),
+        ("ratio_flop_per_byte", ctypes.c_double), ("ratio_mfma_per_load", ctypes.c_double),
+    ]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class SptError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {spt_status_string(status)} ({spt_last_error()})")
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise RuntimeError(f"libspt.so not found at {lib_path}: build it with "
+                               "`python -m software_pipelined_tiling_amd.build`")
+        L = ctypes.CDLL(lib_path)
+        i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        L.spt_gemm.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, vp]
+        L.spt_gemm.restype = i32
+        L.spt_gemm_ex.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, vp, i32, i32, i32, i32]
+        L.spt_gemm_ex.restype = i32
+        L.spt_plan.argtypes = [i32, i64, i64, i64, i32, i32, i32, i32, ctypes.POINTER(PlanInfo)]
+        L.spt_plan.restype = i32
+        L.spt_status_string.argtypes = [i32]
+        L.spt_status_string.restype = ctypes.c_char_p
+        L.spt_last_error.argtypes = []
+        L.spt_last_error.restype = ctypes.c_char_p
+        L.spt_version.argtypes = []
+        L.spt_version.restype = i32
+        _lib = L
+    return _lib
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded ``libspt.so`` (raises if it is missing)."""
+    return _load()
+
+
+# ---- the C ABI, same names ---------------------------------------------------
+
+def spt_gemm(M, N, K, A, lda, B, ldb, C, ldc, dtype, stream=0) -> int:
+    return _load().spt_gemm(M, N, K, A, lda, B, ldb, C, ldc, dtype, stream)
+
+
+def spt_gemm_ex(M, N, K, A, lda, B, ldb, C, ldc, dtype, stream, b_layout, variant, stages,
+                tile_id) -> int:
+    return _load().spt_gemm_ex(M, N, K, A, lda, B, ldb, C, ldc, dtype, stream, b_layout, variant,
+                               stages, tile_id)
+
+
+def spt_plan(dtype, M, N, K, b_layout=ROW, variant=VARIANT_AUTO, stages=0, tile_id=TILE_AUTO):
+    """Returns (status, PlanInfo)."""
+    info = PlanInfo()
+    rc = _load().spt_plan(dtype, M, N, K, b_layout, variant, stages, tile_id, ctypes.byref(info))
+    return rc, info
+
+
+def spt_status_string(status: int) -> str:
+    return _load().spt_status_string(status).decode()
+
+
+def spt_last_error() -> str:
+    return _load().spt_last_error().decode()
+
+
+def spt_version() -> int:
+    return _load().spt_version()
+
+
+# ---- torch convenience ---------------------------------------------------------
+
+def _torch_dtype_code(t):
+    import torch
+    m = {torch.float16: F16, torch.bfloat16: BF16, torch.int8: I8, torch.float32: F32}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def plan(dtype: str | int, M: int, N: int, K: int, *, b_layout: str = "row", variant: str = "auto",
+         stages: int = 0, tile: int = 0) -> dict:
+    d = DTYPE_CODES[dtype] if isinstance(dtype, str) else dtype
+    rc, info = spt_plan(d, M, N, K, COL if b_layout == "col" else ROW, VARIANT_CODES[variant],
+                        stages, tile)
+    if rc != SPT_OK:
+        raise SptError(rc, "spt_plan")
+    return info.as_dict()
+
+
+def gemm(A, B, out=None, *, b_layout: str = "row", variant: str = "auto", stages: int = 0,
+         tile: int = 0, stream=None, K: int | None = None, N: int | None = None):
+    """C = A @ B for torch tensors on the GPU, through ``spt_gemm_ex``.
+
+    A: (M, >=K) with unit column stride (row pitch = A.stride(0)).
+    B: row-major (K, >=N) or, with b_layout='col', (N, >=K) holding B^T.
+    out: (M, >=N) float32 (int32 for int8 inputs); allocated when None.
+    K / N default to the operand widths; pass them to treat the rest of each
+    row as padding.
+    """
+    import torch
+    if A.dtype != B.dtype:
+        raise TypeError("A and B must have the same dtype")
+    d = _torch_dtype_code(A)
+    if A.dim() != 2 or B.dim() != 2 or A.stride(1) != 1 or B.stride(1) != 1:
+        raise ValueError("A and B must be 2-D with unit column stride")
+    col = b_layout == "col"
+    M = A.shape[0]
+    K = A.shape[1] if K is None else K
+    if N is None:
+        N = B.shape[0] if col else B.shape[1]
+    if out is None:  # row pitch padded to 16 bytes; the result is the (M, N) view
+        ldc = -(-max(N, 1) // 4) * 4
+        out = torch.empty((M, ldc), dtype=torch.int32 if d == I8 else torch.float32,
+                          device=A.device)[:, :N]
+    if out.dim() != 2 or out.stride(1) != 1 or out.shape[0] != M or out.shape[1] < N:
+        raise ValueError("out must be (M, >=N) with unit column stride")
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+    rc = spt_gemm_ex(M, N, K, A.data_ptr(), A.stride(0), B.data_ptr(), B.stride(0), out.data_ptr(),
+                     out.stride(0), d, stream, COL if col else ROW, VARIANT_CODES[variant], stages,
+                     tile)
+    if rc != SPT_OK:
+        raise SptError(rc, "spt_gemm_ex")
+    return out

@@ -1,0 +1,68 @@
+"""Build libspt.so (the gfx950 HIP kernels + the C ABI of include/spt.h).
+
+Every translation unit is compiled by hipcc for gfx950 in parallel, then
+linked into ``software_pipelined_tiling_amd/libspt.so`` (in-tree).
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(HERE, "libspt.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+SOURCES = ["spt_kernels_f16.hip", "spt_kernels_bf16.hip", "spt_kernels_i8.hip",
+           "spt_kernels_f32.hip", "spt_api.cpp"]
+HEADERS = ["spt_kernel.hpp", "spt_instances.hpp", "spt_registry.h", "spt_config.h"]
+
+# Packed-fp32 VALU instructions are disabled for all device code (-packed-fp32-ops).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-command-line-argument"]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-4000:]}")
+    return obj
+
+
+def build(jobs: int | None = None, verbose: bool = True) -> str:
+    """Compile every source for gfx950 and link libspt.so; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr[-4000:]}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}", file=sys.stderr)
+    return LIB
+
+
+def asm(src: str = "spt_kernels_f16.hip", out: str | None = None) -> str:
+    """gfx950 assembly of one kernel translation unit (for the ISA checks)."""
+    os.makedirs(BUILD, exist_ok=True)
+    out = out or os.path.join(BUILD, os.path.splitext(src)[0] + ".s")
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stderr[-4000:]}")
+    return out
+
+
+if __name__ == "__main__":
+    build()

@@ -1,0 +1,219 @@
+// spt_api.cpp -- the C ABI of libspt: argument validation, planning and
+// dispatch of the K-loop kernels (declared in include/spt.h).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/spt.h"
+#include "spt_config.h"
+#include "spt_registry.h"
+
+namespace spt {
+
+static thread_local char g_last_error[256] = "";
+
+static int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+static int fail(int status, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+static const KernelTable& table_for(int dtype)
+{
+    static const KernelTable t[4] = {kernels_f16(), kernels_bf16(), kernels_i8(), kernels_f32()};
+    return t[dtype];
+}
+
+const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int stages)
+{
+    if (dtype < 0 || dtype > 3) return nullptr;
+    const KernelTable& t = table_for(dtype);
+    for (int i = 0; i < t.count; ++i) {
+        const KernelEntry& e = t.entries[i];
+        if (e.bcol == bcol && e.tile == tile && e.variant == variant && e.stages == stages) return &e;
+    }
+    return nullptr;
+}
+
+// The library's default when the caller passes AUTO: the 3-stage DIRECT ring
+// on the 128 x 256 tile.
+static void resolve(int& variant, int& stages, int& tile)
+{
+    if (tile == 0) tile = 1;
+    if (variant == V_AUTO) variant = V_DIRECT;
+    if (stages == 0) stages = variant == V_SYNC ? 1 : variant == V_REG ? 2 : (tile == 2 ? 2 : 3);
+}
+
+static bool valid_pair(int variant, int stages)
+{
+    return (variant == V_SYNC && stages == 1) || (variant == V_REG && (stages == 1 || stages == 2)) ||
+           (variant == V_DIRECT && (stages == 2 || stages == 3));
+}
+
+// Checks every argument except the pointers; fills `pi` on success.
+static int make_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, int variant,
+                     int stages, int tile, spt_plan_info* pi)
+{
+    if (dtype < 0 || dtype > 3) return fail(SPT_ERR_INVALID, "dtype %d is not an spt_dtype", dtype);
+    if (b_layout != SPT_ROW && b_layout != SPT_COL)
+        return fail(SPT_ERR_INVALID, "b_layout %d is not an spt_layout", b_layout);
+    if (variant < 0 || variant > 3) return fail(SPT_ERR_INVALID, "variant %d is not an spt_variant", variant);
+    if (stages < 0 || stages > 3) return fail(SPT_ERR_INVALID, "stages %d not in 0..3", stages);
+    if (tile < 0 || tile >= kNumTiles) return fail(SPT_ERR_INVALID, "tile_id %d is not an spt_tile", tile);
+    if (M < 0 || N < 0 || K < 0) return fail(SPT_ERR_INVALID, "negative size");
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(SPT_ERR_UNSUPPORTED, "size above 2^31-1");
+    if (dtype == DT_I8 && K > 131071)
+        return fail(SPT_ERR_UNSUPPORTED, "int8 K=%lld exceeds 131071 (exact int32 sum)", (long long)K);
+    resolve(variant, stages, tile);
+    if (!valid_pair(variant, stages))
+        return fail(SPT_ERR_UNSUPPORTED, "variant %d has no %d-stage form", variant, stages);
+
+    const TileShape& T = kTiles[tile];
+    const int elt = elt_bytes(dtype);
+    spt_plan_info p;
+    memset(&p, 0, sizeof p);
+    p.dtype = dtype;
+    p.b_layout = b_layout;
+    p.variant = variant;
+    p.stages = stages;
+    p.tile_id = tile;
+    p.BM = T.BM;
+    p.BN = T.BN;
+    p.BK = T.BKB / elt;
+    p.waves = T.WAVES_M * T.WAVES_N;
+    p.threads = kWaveSize * p.waves;
+    p.wave_m = T.BM / T.WAVES_M;
+    p.wave_n = T.BN / T.WAVES_N;
+    p.elt_bytes = elt;
+    p.tiles_m = (M + T.BM - 1) / T.BM;
+    p.tiles_n = (N + T.BN - 1) / T.BN;
+    p.grid = p.tiles_m * p.tiles_n;
+    p.k_tiles = (K + p.BK - 1) / p.BK;
+    p.k_full_tiles = K / p.BK;
+    p.k_tail = (int32_t)(K - p.k_full_tiles * p.BK);
+    // "Pipeline GPU Kernel", Schritt 1: smem_a = BM*BK*sizeof(T), smem_b = BK*BN*sizeof(T).
+    p.a_stage_bytes = p.BM * p.BK * elt;
+    p.b_stage_bytes = p.BK * p.BN * elt;
+    p.stage_bytes = p.a_stage_bytes + p.b_stage_bytes;
+    p.lds_bytes = stages * p.stage_bytes;
+    // "Hiding Memory Latency ...", section 6: 16-byte accesses per thread per stage.
+    p.a_copies_per_thread = p.a_stage_bytes / 16 / p.threads;
+    p.b_copies_per_thread = p.b_stage_bytes / 16 / p.threads;
+    // "Kernel-Engpass analysieren", Schritt 3 / 6: the LDS limit on resident workgroups.
+    p.wg_per_cu_lds = kLdsPerCu / p.lds_bytes;
+    p.waves_per_simd_lds = p.wg_per_cu_lds * p.waves / kSimdsPerCu;
+    p.steady_vmcnt = variant == V_DIRECT ? (stages - 2) * (p.a_copies_per_thread + p.b_copies_per_thread) : 0;
+    // one 16x16 MFMA step covers 64 bytes of k per lane group; fp32 issues 4 MFMAs per step
+    const int kstep = 4 * (16 / elt);
+    p.mfma_per_ktile_per_wave = (p.wave_m / 16) * (p.wave_n / 16) * (p.BK / kstep) * (dtype == DT_F32 ? 4 : 1);
+    // "Pipeline GPU Kernel", Schritt 2: 2*BM*BN*BK / ((BM*BK + BK*BN) * sizeof(T)).
+    p.ratio_flop_per_byte = (2.0 * p.BM * p.BN * p.BK) / ((double)(p.BM * p.BK + p.BK * p.BN) * elt);
+    // "Kernel-Engpass analysieren", Schritt 4: compute instructions per load instruction.
+    p.ratio_mfma_per_load =
+        (double)p.mfma_per_ktile_per_wave / (double)(p.a_copies_per_thread + p.b_copies_per_thread);
+    *pi = p;
+    return SPT_OK;
+}
+
+static int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                     int64_t ldb, void* C, int64_t ldc, int dtype, void* stream, int b_layout,
+                     int variant, int stages, int tile)
+{
+    spt_plan_info pi;
+    int rc = make_plan(dtype, M, N, K, b_layout, variant, stages, tile, &pi);
+    if (rc != SPT_OK) return rc;
+    if (M == 0 || N == 0) return SPT_OK;
+
+    const int elt = pi.elt_bytes;
+    const bool bcol = b_layout == SPT_COL;
+    if (!C) return fail(SPT_ERR_INVALID, "C is null");
+    if (K > 0 && (!A || !B)) return fail(SPT_ERR_INVALID, "A or B is null");
+    const int64_t kmin = K > 0 ? K : 1;
+    if (lda < kmin) return fail(SPT_ERR_INVALID, "lda=%lld < K", (long long)lda);
+    if (bcol ? ldb < kmin : ldb < N) return fail(SPT_ERR_INVALID, "ldb=%lld too small", (long long)ldb);
+    if (ldc < N) return fail(SPT_ERR_INVALID, "ldc=%lld < N", (long long)ldc);
+    if (lda > INT32_MAX || ldb > INT32_MAX || ldc > INT32_MAX)
+        return fail(SPT_ERR_UNSUPPORTED, "row pitch above 2^31-1");
+    if (((uintptr_t)C % 16) || (ldc * 4) % 16) return fail(SPT_ERR_MISALIGNED, "C or ldc not 16-byte aligned");
+    if (K > 0 && (((uintptr_t)A % 16) || ((uintptr_t)B % 16) || (lda * elt) % 16 || (ldb * elt) % 16))
+        return fail(SPT_ERR_MISALIGNED, "A, B, lda or ldb not 16-byte aligned");
+    // Byte offsets inside one workgroup's operand panel are 32-bit buffer offsets.
+    const int64_t lim = INT64_C(0x7ffffff0);
+    if ((int64_t)pi.BM * lda * elt >= lim || (bcol ? (int64_t)pi.BN * ldb * elt : (int64_t)pi.BK * ldb * elt) >= lim)
+        return fail(SPT_ERR_UNSUPPORTED, "operand panel exceeds 2 GiB of buffer offsets");
+    if (pi.grid > INT32_MAX) return fail(SPT_ERR_UNSUPPORTED, "too many workgroups");
+
+    const KernelEntry* e = find_kernel(dtype, bcol, pi.tile_id, pi.variant, pi.stages);
+    if (!e) return fail(SPT_ERR_UNSUPPORTED, "no kernel built for dtype %d layout %d tile %d variant %d stages %d",
+                        dtype, b_layout, pi.tile_id, pi.variant, pi.stages);
+
+    GemmArgs a;
+    a.A = (const char*)A;
+    a.B = (const char*)B;
+    a.C = (char*)C;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.lda = (int)lda;
+    a.ldb = (int)ldb;
+    a.ldc = (int)ldc;
+    a.tiles_m = (int)pi.tiles_m;
+    a.tiles_n = (int)pi.tiles_n;
+    a.k_full = (int)pi.k_full_tiles;
+    a.k_tail = pi.k_tail;
+    const hipError_t err = e->launch(a, (unsigned)pi.grid, (hipStream_t)stream);
+    if (err != hipSuccess) return fail(SPT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(err));
+    g_last_error[0] = 0;
+    return SPT_OK;
+}
+
+}  // namespace spt
+
+extern "C" {
+
+int spt_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+             void* C, int64_t ldc, int dtype, void* stream)
+{
+    return spt::gemm_impl(M, N, K, A, lda, B, ldb, C, ldc, dtype, stream, SPT_ROW, SPT_VARIANT_AUTO, 0,
+                          SPT_TILE_AUTO);
+}
+
+int spt_gemm_ex(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                void* C, int64_t ldc, int dtype, void* stream, int b_layout, int variant, int stages,
+                int tile_id)
+{
+    return spt::gemm_impl(M, N, K, A, lda, B, ldb, C, ldc, dtype, stream, b_layout, variant, stages,
+                          tile_id);
+}
+
+int spt_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, int variant, int stages,
+             int tile_id, spt_plan_info* out)
+{
+    if (!out) return spt::fail(SPT_ERR_INVALID, "out is null");
+    return spt::make_plan(dtype, M, N, K, b_layout, variant, stages, tile_id, out);
+}
+
+const char* spt_status_string(int status)
+{
+    switch (status) {
+    case SPT_OK: return "SPT_OK";
+    case SPT_ERR_INVALID: return "SPT_ERR_INVALID";
+    case SPT_ERR_UNSUPPORTED: return "SPT_ERR_UNSUPPORTED";
+    case SPT_ERR_MISALIGNED: return "SPT_ERR_MISALIGNED";
+    case SPT_ERR_LAUNCH: return "SPT_ERR_LAUNCH";
+    default: return "SPT_ERR_UNKNOWN";
+    }
+}
+
+const char* spt_last_error(void) { return spt::g_last_error; }
+
+int spt_version(void) { return SPT_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// spt_instances.hpp -- explicit instantiations of the K-loop kernel for one
+// element type.  Included once per element type so the translation units
+// compile in parallel.
+#pragma once
+
+#include "spt_kernel.hpp"
+#include "spt_registry.h"
+
+namespace spt {
+
+template <class C>
+hipError_t launch_gemm(const GemmArgs& a, unsigned grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL(gemm_kernel<C>, dim3(grid), dim3(C::THREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int DT, int BC, int TI, int V, int S>
+constexpr KernelEntry entry()
+{
+    typedef Cfg<DT, BC != 0, TI, V, S> C;
+    return KernelEntry{DT, BC, TI, V, S, C::THREADS, C::LDS_BYTES, C::LOADS, &launch_gemm<C>,
+                       (const void*)&gemm_kernel<C>};
+}
+
+// Every (variant, stages) pair of the boundary for one (dtype, layout, tile).
+#define SPT_PAIRS(DT, BC, TI)                                                              \
+    entry<DT, BC, TI, V_SYNC, 1>(), entry<DT, BC, TI, V_REG, 1>(), entry<DT, BC, TI, V_REG, 2>(), \
+        entry<DT, BC, TI, V_DIRECT, 2>()
+// The 3-stage ring where it fits in LDS (the 256 x 256 tile needs 3 x 64 KiB).
+#define SPT_RING3(DT, BC, TI) entry<DT, BC, TI, V_DIRECT, 3>()
+
+#define SPT_DEFINE_TABLE(NAME, DT)                                                          \
+    static const KernelEntry k_##NAME[] = {                                                \
+        SPT_PAIRS(DT, 0, 1), SPT_RING3(DT, 0, 1), SPT_PAIRS(DT, 1, 1), SPT_RING3(DT, 1, 1), \
+        SPT_PAIRS(DT, 0, 2), SPT_PAIRS(DT, 1, 2),                                          \
+        SPT_PAIRS(DT, 0, 3), SPT_RING3(DT, 0, 3), SPT_PAIRS(DT, 1, 3), SPT_RING3(DT, 1, 3), \
+    };                                                                                     \
+    KernelTable kernels_##NAME() { return KernelTable{k_##NAME, (int)(sizeof(k_##NAME) / sizeof(k_##NAME[0]))}; }
+
+}  // namespace spt

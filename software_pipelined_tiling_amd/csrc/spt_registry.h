@@ -1,0 +1,33 @@
+// spt_registry.h -- the built (dtype, B layout, tile, variant, stages)
+// instantiations of the K-loop kernel and their launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "spt_config.h"
+
+namespace spt {
+
+typedef hipError_t (*LaunchFn)(const GemmArgs&, unsigned grid, hipStream_t);
+
+struct KernelEntry {
+    int dtype, bcol, tile, variant, stages;
+    int threads, lds_bytes, loads_per_tile;
+    LaunchFn launch;
+    const void* kernel;
+};
+
+struct KernelTable {
+    const KernelEntry* entries;
+    int count;
+};
+
+KernelTable kernels_f16();
+KernelTable kernels_bf16();
+KernelTable kernels_i8();
+KernelTable kernels_f32();
+
+// nullptr when that combination is not built.
+const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int stages);
+
+}  // namespace spt

@@ -17,3 +17,12 @@ def oracle_mod():
     from oracle import oracle as o
     o.build(force=False)
     return o
+
+
+@pytest.fixture(scope="session")
+def built_lib():
+    """libspt.so as built in-tree; built here only when it is missing."""
+    from software_pipelined_tiling_amd import build as b
+    if not os.path.exists(b.LIB):
+        b.build()
+    return b.LIB

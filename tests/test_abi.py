@@ -1,0 +1,129 @@
+"""The C-ABI library without a GPU: it loads, exports every declared entry point,
+rejects bad arguments before touching a device, and its planner agrees with the
+pages' formulas (restated in oracle/plan_oracle.py)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import software_pipelined_tiling_amd as spt
+from oracle import plan_oracle as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L(built_lib):
+    return spt.lib()
+
+
+def declared_functions():
+    txt = open(os.path.join(ROOT, "include", "spt.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(spt_\w+)\s*\(", txt, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert names == sorted(["spt_gemm", "spt_gemm_ex", "spt_plan", "spt_status_string",
+                            "spt_last_error", "spt_version"])
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert spt.spt_version() == 10000
+    assert spt.spt_status_string(0) == "SPT_OK"
+    assert spt.spt_status_string(-1) == "SPT_ERR_INVALID"
+    assert spt.spt_status_string(-2) == "SPT_ERR_UNSUPPORTED"
+    assert spt.spt_status_string(-3) == "SPT_ERR_MISALIGNED"
+    assert spt.spt_status_string(-4) == "SPT_ERR_LAUNCH"
+    assert spt.spt_status_string(99) == "SPT_ERR_UNKNOWN"
+
+
+# Fake but aligned device addresses: every call below must fail validation
+# before any HIP call, so nothing is ever dereferenced.
+PA, PB, PC = 0x10000, 0x20000, 0x30000
+
+
+def ex(M=64, N=64, K=64, A=PA, lda=None, B=PB, ldb=None, C=PC, ldc=None, dtype=spt.F16, lay=spt.ROW,
+       var=spt.VARIANT_AUTO, st=0, tile=0):
+    lda = K if lda is None else lda
+    ldb = (K if lay == spt.COL else N) if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return spt.spt_gemm_ex(M, N, K, A, lda, B, ldb, C, ldc, dtype, 0, lay, var, st, tile)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), -1), (dict(lay=2), -1), (dict(var=9), -1), (dict(st=4), -1), (dict(tile=9), -1),
+    (dict(M=-1), -1), (dict(K=-5), -1), (dict(C=0), -1), (dict(A=0), -1), (dict(B=0), -1),
+    (dict(lda=32), -1), (dict(ldb=32), -1), (dict(ldc=8), -1), (dict(lay=spt.COL, ldb=32), -1),
+    (dict(var=spt.VARIANT_SYNC, st=2), -2), (dict(var=spt.VARIANT_DIRECT, st=1), -2),
+    (dict(var=spt.VARIANT_REG, st=3), -2), (dict(dtype=spt.I8, K=131072), -2),
+    (dict(var=spt.VARIANT_DIRECT, st=3, tile=spt.TILE_256x256), -2),
+    (dict(A=PA + 8), -3), (dict(B=PB + 2), -3), (dict(C=PC + 4), -3),
+    (dict(K=60, lda=60), -3), (dict(N=60, ldb=60, ldc=64), -3), (dict(N=62, ldc=62), -3),
+])
+def test_validation_errors(L, kw, status):
+    assert ex(**kw) == status
+    assert spt.spt_last_error() != ""
+
+
+def test_empty_problem_is_ok_without_launch(L):
+    assert ex(M=0) == 0
+    assert ex(N=0, ldb=1, ldc=1) == 0
+    assert spt.spt_gemm(0, 0, 0, 0, 1, 0, 1, 0, 1, spt.F16, 0) == 0
+
+
+def test_plan_rejects_what_gemm_rejects(L):
+    rc, _ = spt.spt_plan(spt.I8, 64, 64, 200000)
+    assert rc == -2
+    rc, _ = spt.spt_plan(5, 64, 64, 64)
+    assert rc == -1
+    assert L.spt_plan(0, 1, 1, 1, 0, 0, 0, 0, None) == -1
+
+
+DTYPES = [(spt.F16, 2), (spt.BF16, 2), (spt.I8, 1), (spt.F32, 4)]
+PAIRS = [(spt.VARIANT_SYNC, 1), (spt.VARIANT_REG, 1), (spt.VARIANT_REG, 2), (spt.VARIANT_DIRECT, 2),
+         (spt.VARIANT_DIRECT, 3)]
+TILES = {1: (128, 256, 64, 256), 2: (256, 256, 128, 512), 3: (128, 128, 64, 256)}
+
+
+@pytest.mark.parametrize("dtype,elt", DTYPES)
+@pytest.mark.parametrize("tile", [1, 2, 3])
+@pytest.mark.parametrize("var,st", PAIRS)
+def test_plan_matches_page_formulas(L, dtype, elt, tile, var, st):
+    BM, BN, BKB, thr = TILES[tile]
+    BK = BKB // elt
+    M, N, K = 4000, 3000, 1000
+    rc, pi = spt.spt_plan(dtype, M, N, K, spt.ROW, var, st, tile)
+    if tile == 2 and st == 3:
+        assert rc == 0  # the plan exists; the kernel is not built (160 KiB LDS)
+    assert rc == 0
+    assert (pi.BM, pi.BN, pi.BK, pi.threads) == (BM, BN, BK, thr)
+    assert pi.stage_bytes == P.stage_bytes(BM, BN, BK, elt)
+    assert pi.a_stage_bytes == BM * BK * elt and pi.b_stage_bytes == BK * BN * elt
+    assert pi.lds_bytes == P.ring_bytes(BM, BN, BK, elt, st)
+    assert pi.a_copies_per_thread == P.copies_per_thread(BM, BK, elt, thr)
+    assert pi.b_copies_per_thread == P.copies_per_thread(BK, BN, elt, thr)
+    assert pi.ratio_flop_per_byte == pytest.approx(P.compute_load_ratio(BM, BN, BK, elt), rel=1e-12)
+    gfx950 = P.Machine(regs_per_sm=4 * 512 * 64, smem_per_sm=163840, max_warps_per_sm=32,
+                       max_blocks_per_sm=32, warp_size=64)
+    blocks, _, lim = P.occupancy(gfx950, 0, pi.lds_bytes, thr)
+    assert pi.wg_per_cu_lds == lim["smem"]
+    assert pi.tiles_m == -(-M // BM) and pi.tiles_n == -(-N // BN) and pi.grid == pi.tiles_m * pi.tiles_n
+    assert pi.k_tiles == -(-K // BK) and pi.k_full_tiles == K // BK and pi.k_tail == K % BK
+    expect_vm = (st - 2) * (pi.a_copies_per_thread + pi.b_copies_per_thread) if var == spt.VARIANT_DIRECT else 0
+    assert pi.steady_vmcnt == expect_vm
+
+
+def test_pages_tile_plan(L):
+    """The 128 x 256 x 32 fp16 tile with 256 threads and 3 stages: 24 KiB per stage,
+    72 KiB in all, 2 + 4 sixteen-byte copies per thread per stage."""
+    rc, pi = spt.spt_plan(spt.F16, 4096, 4096, 4096, spt.ROW, spt.VARIANT_DIRECT, 3, 1)
+    assert rc == 0
+    assert (pi.stage_bytes, pi.lds_bytes) == (24576, 73728)
+    assert (pi.a_copies_per_thread, pi.b_copies_per_thread) == (2, 4)
+    assert pi.wg_per_cu_lds == 2 and pi.steady_vmcnt == 6
+    assert pi.grid == 512 and pi.k_tiles == 128

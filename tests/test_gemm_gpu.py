@@ -1,0 +1,263 @@
+"""Parity of the HIP K-loop (through the C ABI) with the CPU oracle, on an MI355X.
+
+Float results must be within the normalised tolerance of tests/parity.py;
+int8 results must be bit-exact; closed forms and integer-valued inputs must
+be bit-exact for every dtype; every (variant, stages) pair of one tile must
+produce bit-identical C ("Pipeline GPU Kernel", Schritt 5: pipelining only
+reorders the loads).  C is pre-filled with a sentinel so an unwritten output
+or a write outside M x N shows up.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import software_pipelined_tiling_amd as spt
+from software_pipelined_tiling_amd import inputs as I
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+PAIRS = [("sync", 1), ("reg", 1), ("reg", 2), ("direct", 2), ("direct", 3)]
+TILES = [1, 2, 3]
+SENT_F = np.uint32(0x7FC00ABC)   # a NaN payload no kernel produces
+SENT_I = np.int32(0x7FFFFFFF)
+
+
+def built(tile, variant, stages):
+    return not (tile == 2 and variant == "direct" and stages == 3)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu(built_lib):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    spt.lib()
+
+
+def to_dev(x: np.ndarray, dtype: str):
+    if dtype in ("f16", "bf16"):
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16).copy())
+        t = t.view(torch.float16 if dtype == "f16" else torch.bfloat16)
+    elif dtype == "f32":
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32).copy())
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.int8).copy())
+    return t.to("cuda")
+
+
+def alloc_c(M, ldc, dtype):
+    if dtype == "i8":
+        return torch.full((M, ldc), int(SENT_I), dtype=torch.int32, device="cuda")
+    return torch.full((M, ldc), int(SENT_F), dtype=torch.int32, device="cuda").view(torch.float32)
+
+
+def launch(dA, dB, C, dtype, M, N, K, lda, ldb, b_col, variant="auto", stages=0, tile=0, stream=None):
+    s = torch.cuda.current_stream().cuda_stream if stream is None else stream.cuda_stream
+    rc = spt.spt_gemm_ex(M, N, K, dA.data_ptr(), lda, dB.data_ptr(), ldb, C.data_ptr(), C.shape[1],
+                         spt.DTYPE_CODES[dtype], s, spt.COL if b_col else spt.ROW,
+                         spt.VARIANT_CODES[variant], stages, tile)
+    assert rc == 0, f"{spt.spt_status_string(rc)}: {spt.spt_last_error()}"
+
+
+def run(A, B, dtype, b_col, M, N, K, variant="auto", stages=0, tile=0, ldc_pad=4):
+    """Launch once; return the host copy of C[:, :N], checking the padding kept its sentinel."""
+    print(f"[gpu] {dtype} {'col' if b_col else 'row'} M={M} N={N} K={K} lda={A.shape[1]} "
+          f"ldb={B.shape[1]} {variant}/{stages} tile={tile}", flush=True)
+    dA, dB = to_dev(A, dtype), to_dev(B, dtype)
+    ldc = -(-(N + ldc_pad) // 4) * 4  # 16-byte row pitch
+    C = alloc_c(M, ldc, dtype)
+    launch(dA, dB, C, dtype, M, N, K, A.shape[1], B.shape[1], b_col, variant, stages, tile)
+    torch.cuda.synchronize()
+    h = C.cpu().numpy()
+    pad = h[:, N:].view(np.int32)
+    want = SENT_I if dtype == "i8" else np.array(SENT_F).view(np.int32)
+    assert np.all(pad == want), "write outside M x N"
+    return np.ascontiguousarray(h[:, :N])
+
+
+def operands(dtype, b_col, M, N, K, seed, lda_pad=0, ldb_pad=0, dist="uniform", lo=-1.0, hi=1.0,
+             pad_nan=True):
+    """Seeded operands with padded row pitches; padding holds NaN (int8: 127) so any
+    leak of padding into the product is visible."""
+    if dtype == "i8":
+        lo, hi = -128, 127
+    e = I.ELT_BYTES[dtype]
+    q = 16 // e  # elements per 16 bytes: pitches stay 16-byte multiples
+    lda = -(-(K + lda_pad) // q) * q if K else q
+    bw = K if b_col else N
+    ldb = -(-(bw + ldb_pad) // q) * q if bw else q
+    w = I.Workload("t", seed, dtype, M, N, K, b_col, dist, lo, hi)
+    a, b = I.make_operands(w, lda=lda, ldb=ldb)
+    if pad_nan:
+        fill = {"f16": 0x7E00, "bf16": 0x7FC0, "f32": np.nan, "i8": 127}[dtype]
+        a[:, K:] = fill
+        b[:, bw:] = fill
+    return a, b
+
+
+def ref(oracle_mod, A, B, dtype, b_col, N, K):
+    return oracle_mod.gemm(A, B, dtype, b_col=b_col, K=K, N=N)
+
+
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("tile", TILES)
+def test_fp16_256_all_variants(oracle_mod, tile):
+    """fp16 256^3, U[-1,1] (the small headline workload): every (variant, stages) pair
+    matches the oracle and all of them are bit-identical."""
+    w = I.W_F16_256
+    A, B = I.make_operands(w)
+    Cref = ref(oracle_mod, A, B, "f16", False, w.N, w.K)
+    outs = {}
+    for v, s in PAIRS:
+        if not built(tile, v, s):
+            continue
+        outs[(v, s)] = run(A, B, "f16", False, w.M, w.N, w.K, v, s, tile)
+        parity.check_full(outs[(v, s)], Cref, A, B, "f16", False, w.M, w.N, w.K)
+    first = next(iter(outs.values()))
+    for k, o in outs.items():
+        assert np.array_equal(o.view(np.uint32), first.view(np.uint32)), f"{k} differs from {PAIRS[0]}"
+
+
+SHAPES = [(1, 1, 1), (15, 17, 33), (17, 15, 8), (127, 129, 95), (129, 257, 161), (64, 64, 31),
+          (64, 64, 33), (64, 64, 63), (64, 64, 65), (257, 300, 1000), (300, 520, 4)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8", "f32"])
+@pytest.mark.parametrize("b_col", [False, True])
+def test_ragged_shapes(oracle_mod, dtype, b_col):
+    """Shapes that are not tile multiples, K tails of every width, padded pitches
+    with NaN padding; default variant plus the unpipelined one."""
+    for i, (M, N, K) in enumerate(SHAPES):
+        A, B = operands(dtype, b_col, M, N, K, 100 + i, lda_pad=3, ldb_pad=5)
+        Cref = ref(oracle_mod, A, B, dtype, b_col, N, K)
+        for v, s in [("auto", 0), ("sync", 1)]:
+            C = run(A, B, dtype, b_col, M, N, K, v, s)
+            parity.check_full(C, Cref, A, B, dtype, b_col, M, N, K)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8", "f32"])
+@pytest.mark.parametrize("b_col", [False, True])
+@pytest.mark.parametrize("tile", TILES)
+def test_variants_bit_identical_ragged(oracle_mod, dtype, b_col, tile):
+    """A ragged problem spanning several tiles in M, N and K: all variants agree
+    with the oracle and with each other bit for bit."""
+    M, N, K = 300, 600, 333 if dtype != "f32" else 300
+    A, B = operands(dtype, b_col, M, N, K, 7, lda_pad=8, ldb_pad=8)
+    Cref = ref(oracle_mod, A, B, dtype, b_col, N, K)
+    outs = []
+    for v, s in PAIRS:
+        if not built(tile, v, s):
+            continue
+        C = run(A, B, dtype, b_col, M, N, K, v, s, tile)
+        parity.check_full(C, Cref, A, B, dtype, b_col, M, N, K)
+        outs.append(C)
+    for C in outs[1:]:
+        assert np.array_equal(C.view(np.uint32), outs[0].view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+def test_integer_valued_bit_exact(oracle_mod, dtype):
+    """Integer inputs (|a|,|b| <= 4; int8 full range): every partial sum is exact in the
+    accumulator, so C equals the oracle bit for bit."""
+    M, N, K = 384, 512, 1024
+    lo, hi = (-4, 4) if dtype != "i8" else (-128, 127)
+    w = I.Workload("int", 21, dtype, M, N, K, False, "intgrid", lo, hi)
+    A, B = I.make_operands(w)
+    Cref = ref(oracle_mod, A, B, dtype, False, N, K)
+    for v, s in [("direct", 3), ("reg", 2), ("sync", 1)]:
+        C = run(A, B, dtype, False, M, N, K, v, s)
+        assert np.array_equal(C.astype(np.float64), Cref.astype(np.float64))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32", "i8"])
+@pytest.mark.parametrize("b_col", [False, True])
+def test_identity_and_permutation(dtype, b_col):
+    """A * I == A and A * P permutes the columns of A, exactly, on the GPU."""
+    M, K = 200, 320
+    lo, hi = (-128, 127) if dtype == "i8" else (-1, 1)
+    A = I.draw("uniform", lo, hi, (M, K), np.random.default_rng(5), dtype)
+    Av = parity.values(A, dtype)
+    from tests.oracle_pins import _store
+    eye = _store(np.eye(K), dtype)
+    pi = [(k + 37) % K for k in range(K)]
+    Pm = np.zeros((K, K))
+    for k in range(K):
+        Pm[k, pi[k]] = 1.0
+    P = _store(Pm, dtype)
+    for Bm, want in [(eye, Av), (P, Av[:, np.argsort(pi)])]:
+        Bs = np.ascontiguousarray(Bm.T) if b_col else Bm
+        C = run(A, Bs, dtype, b_col, M, K, K)
+        assert np.array_equal(C.astype(np.float64), want)
+
+
+def test_k_zero_writes_zeros():
+    A = np.zeros((70, 8), dtype=np.uint16)
+    B = np.zeros((1, 264), dtype=np.uint16)
+    C = run(A, B, "f16", False, 70, 260, 0)
+    assert np.all(C == 0)
+
+
+def test_non_default_stream(oracle_mod):
+    M, N, K = 256, 512, 512
+    A, B = operands("bf16", False, M, N, K, 9)
+    Cref = ref(oracle_mod, A, B, "bf16", False, N, K)
+    dA, dB = to_dev(A, "bf16"), to_dev(B, "bf16")
+    C = alloc_c(M, N, "bf16")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        launch(dA, dB, C, "bf16", M, N, K, A.shape[1], B.shape[1], False, stream=s)
+    s.synchronize()
+    parity.check_full(C.cpu().numpy(), Cref, A, B, "bf16", False, M, N, K)
+
+
+def test_torch_wrapper(oracle_mod):
+    M, N, K = 130, 250, 96
+    A, B = operands("f16", True, M, N, K, 13, pad_nan=False)
+    Cref = ref(oracle_mod, A, B, "f16", True, N, K)
+    out = spt.gemm(to_dev(A, "f16"), to_dev(B, "f16"), b_layout="col", K=K, N=N)
+    torch.cuda.synchronize()
+    parity.check_full(out.cpu().numpy(), Cref, A, B, "f16", True, M, N, K)
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, in the launch configurations the benchmark times;
+# sampled outputs are recomputed one by one by the oracle.
+
+def sampled(oracle_mod, w: I.Workload, variant="auto", stages=0, tile=0, n=3000):
+    print(f"[gpu] full-size {w.name} {variant}/{stages} tile={tile}", flush=True)
+    A, B = I.make_operands(w)
+    dA, dB = to_dev(A, w.dtype), to_dev(B, w.dtype)
+    C = alloc_c(w.M, w.N, w.dtype)
+    launch(dA, dB, C, w.dtype, w.M, w.N, w.K, A.shape[1], B.shape[1], w.b_col, variant, stages, tile)
+    rows, cols = parity.sample_entries(w.M, w.N, n, np.random.default_rng(w.wid))
+    got = C[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()].cpu().numpy()
+    # every output written: no sentinel anywhere
+    if w.dtype == "i8":
+        assert not bool((C == int(SENT_I)).any())
+    else:
+        assert bool(torch.isfinite(C).all())
+    want = oracle_mod.gemm_entries(A, B, w.dtype, rows, cols, b_col=w.b_col, K=w.K)
+    return parity.check_entries(got, want, rows, cols, A, B, w.dtype, w.b_col, w.M, w.N, w.K)
+
+
+@pytest.mark.parametrize("variant,stages", [("auto", 0)] + PAIRS)
+def test_full_fp16_4096(oracle_mod, variant, stages):
+    sampled(oracle_mod, I.W_F16_4096, variant, stages, 1)
+
+
+@pytest.mark.parametrize("variant,stages", [("auto", 0), ("sync", 1), ("direct", 2)])
+def test_full_int8_4096_bcol(oracle_mod, variant, stages):
+    sampled(oracle_mod, I.W_I8_4096, variant, stages, 1)
+
+
+@pytest.mark.parametrize("K", I.LOWK_KS)
+def test_full_bf16_lowk(oracle_mod, K):
+    sampled(oracle_mod, I.w_bf16_lowk(K))
+
+
+@pytest.mark.parametrize("variant,stages", [("auto", 0), ("reg", 2), ("sync", 1)])
+def test_full_bf16_ragged(oracle_mod, variant, stages):
+    sampled(oracle_mod, I.W_BF16_RAGGED, variant, stages)
