@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of the software-pipelined GEMM K-loop on one MI355X.
+
+One step = one C = A*B call of the library on the headline workload (fp16
+GEMM 4096x4096x4096, A and B row-major, fp32 accumulation and fp32 C, entries
+uniform in [-1, 1] rounded to fp16 from a fixed seed), inputs resident in HBM
+before the timed region.  Prints ONE JSON line.
+
+Besides the headline value it reports, in the same line:
+  roofline      the dominant (only) kernel's achieved TFLOP/s against the
+                dense fp16 MFMA peak, timed with HIP events on the stream
+                the kernel runs on; HBM traffic from rocprofv3 counters when
+                a summary taken on the current kernel source is committed
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload
+  sweep         every (tile, variant, stages) of the library on the
+                headline workload, the unpipelined one included
+  workloads     int8 4096^3 (B column-major), bf16 8192^2 x K low-K sweep
+                (with HBM GB/s), bf16 4000x3000x1000 ragged
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "i8": 5033.2, "f32": 157.3}  # dense MFMA, MI355X
+HBM_GBS = 8000.0
+PAIRS = [("sync", 1), ("reg", 1), ("reg", 2), ("direct", 2), ("direct", 3)]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "software_pipelined_tiling_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def to_dev(x: np.ndarray, dtype: str):
+    import torch
+    if dtype in ("f16", "bf16"):
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16).copy())
+        return t.view(torch.float16 if dtype == "f16" else torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x).copy()).cuda()
+
+
+class Problem:
+    """Device-resident operands and output of one workload."""
+
+    def __init__(self, w):
+        import torch
+        from software_pipelined_tiling_amd import inputs as I
+        self.w = w
+        self.A, self.B = I.make_operands(w)
+        self.dA, self.dB = to_dev(self.A, w.dtype), to_dev(self.B, w.dtype)
+        self.C = torch.empty((w.M, w.N), dtype=torch.int32 if w.dtype == "i8" else torch.float32,
+                             device="cuda")
+
+    def args(self, stream, variant="auto", stages=0, tile=0):
+        import software_pipelined_tiling_amd as spt
+        w = self.w
+        return (w.M, w.N, w.K, self.dA.data_ptr(), self.A.shape[1], self.dB.data_ptr(),
+                self.B.shape[1], self.C.data_ptr(), w.N, spt.DTYPE_CODES[w.dtype], stream,
+                spt.COL if w.b_col else spt.ROW, spt.VARIANT_CODES[variant], stages, tile)
+
+
+def time_calls(prob: Problem, steps: int, warmup: int, variant="auto", stages=0, tile=0):
+    """Mean ms per call over `steps` back-to-back calls, HIP events on the launch stream."""
+    import torch
+    import software_pipelined_tiling_amd as spt
+    stream = torch.cuda.current_stream()
+    a = prob.args(stream.cuda_stream, variant, stages, tile)
+    rc = spt.spt_gemm_ex(*a)
+    if rc != 0:
+        return None
+    for _ in range(warmup):
+        spt.spt_gemm_ex(*a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        spt.spt_gemm_ex(*a)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def cpu_baseline(w, budget_s: float):
+    """The CPU oracle (as it stands) on the first rows of the same workload."""
+    from oracle import oracle as O
+    from software_pipelined_tiling_amd import inputs as I
+    A, B = I.make_operands(w)
+    cores = O.max_threads()
+    # calibrate on 128 rows, then one measured run sized to the budget (capped at all rows)
+    t0 = time.perf_counter()
+    O.gemm(np.ascontiguousarray(A[:128]), B, w.dtype, b_col=w.b_col)
+    rate = 128 / max(time.perf_counter() - t0, 1e-3)
+    rows = int(min(w.M, max(16, rate * budget_s)))
+    t0 = time.perf_counter()
+    O.gemm(np.ascontiguousarray(A[:rows]), B, w.dtype, b_col=w.b_col)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": round(flops / dt / 1e9, 2), "unit": "GFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of C ({rows} x {w.N} outputs, full K={w.K}) of {w.name}; "
+                      f"{dt:.1f} s on {cores} threads"}
+
+
+def traffic_from_profile(kernel_sha: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they were
+    taken on this exact kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "hbm_traffic_fp16_4096.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha") != kernel_sha:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed calls first; the GPU's clock settles within ~30 ms of load")
+    ap.add_argument("--tile", type=int, default=0, help="headline tile (0 = library default)")
+    ap.add_argument("--variant", default="auto", help="headline variant (auto/sync/reg/direct)")
+    ap.add_argument("--stages", type=int, default=0, help="headline stages (0 = variant default)")
+    ap.add_argument("--cpu-budget", type=float, default=25.0, help="seconds of oracle CPU work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--only-headline", action="store_true", help="headline workload only (profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run 5 plain 256 MiB device copies (HBM counter scale)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus must be 1 "
+              "(the GEMM shards over output tiles, see the sharding design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import software_pipelined_tiling_amd as spt
+    from software_pipelined_tiling_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    spt.lib()  # fails loudly if libspt.so is missing
+
+    head = Problem(I.W_F16_4096)
+    w = head.w
+    # --- timed region: K back-to-back steps, synchronised on both sides ---
+    ms = time_calls(head, args.steps, args.warmup, args.variant, args.stages, args.tile)
+    if ms is None:
+        print(f"bench.py: headline configuration refused: {spt.spt_last_error()}", file=sys.stderr)
+        sys.exit(1)
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    rc, plan = spt.spt_plan(spt.F16, w.M, w.N, w.K, spt.ROW, spt.VARIANT_CODES[args.variant],
+                            args.stages, args.tile)
+    sha = kernel_source_hash()
+    traffic = traffic_from_profile(sha)
+    out = {
+        "metric": "GEMM TFLOPS/TOPS at 4096^3 fp16 & int8, % of MI355X dense MFMA peak",
+        "value": round(tflops, 1),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name + ", A/B row-major, fp32 accumulate, fp32 C, U[-1,1] fp16",
+                   "tile": f"{plan.BM}x{plan.BN}x{plan.BK}", "threads": plan.threads,
+                   "variant": {1: "sync", 2: "reg", 3: "direct"}[plan.variant],
+                   "stages": plan.stages, "pct_of_peak": round(100 * tflops / PEAK_TFLOPS["f16"], 1)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_TFLOPS["f16"],
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS["f16"], 4),
+                     "traffic": traffic, "kernel_source_sha": sha,
+                     "alg_flop_per_launch": w.flops, "alg_bytes_per_launch": w.alg_bytes},
+    }
+
+    if args.copy_calibration:
+        # a plain copy of known size: 256 MiB read + 256 MiB written per launch
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = src.numel() * 4
+        del src, dst
+
+    if not args.only_headline:
+        steps = max(20, min(args.steps, 100))
+        if not args.no_sweep:
+            sweep = []
+            for tile in (1, 2, 3):
+                for v, s in PAIRS:
+                    t = time_calls(head, steps, 3, v, s, tile)
+                    if t is None:
+                        continue
+                    sweep.append({"tile": tile, "variant": v, "stages": s, "us": round(t * 1e3, 2),
+                                  "tflops": round(w.flops / (t * 1e-3) / 1e12, 1)})
+            out["sweep"] = sweep
+            by = {(d["tile"], d["variant"], d["stages"]): d["tflops"] for d in sweep}
+            base = by.get((1, "sync", 1))
+            if base:
+                out["pipelining_speedup_pages_tile"] = {
+                    f"{v}{s}": round(by[(1, v, s)] / base, 3) for v, s in PAIRS if (1, v, s) in by}
+        del head
+        extra = {}
+        for wk in [I.W_I8_4096, I.W_BF16_RAGGED, I.W_F16_256] + [I.w_bf16_lowk(k) for k in I.LOWK_KS]:
+            p = Problem(wk)
+            t = time_calls(p, steps, 3)
+            t1 = time_calls(p, steps, 3, "sync", 1)
+            peak = PEAK_TFLOPS[wk.dtype]
+            tf = wk.flops / (t * 1e-3) / 1e12
+            extra[wk.name] = {"us": round(t * 1e3, 2), "tflops": round(tf, 1),
+                              "pct_of_peak": round(100 * tf / peak, 1),
+                              "hbm_gbs_alg": round(wk.alg_bytes / (t * 1e-3) / 1e9, 1),
+                              "pct_of_hbm": round(100 * wk.alg_bytes / (t * 1e-3) / 1e9 / HBM_GBS, 1),
+                              "unpipelined_us": round(t1 * 1e3, 2),
+                              "speedup_vs_unpipelined": round(t1 / t, 3)}
+            del p
+        out["workloads"] = extra
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(I.W_F16_4096, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -94,12 +94,15 @@ enum spt_variant {
  *                    tile of "Hiding Memory Latency ...", section 6.
  *  SPT_TILE_256x256  256 x 256, 512 threads (2 x 4 waves of 128 x 64).
  *  SPT_TILE_128x128  128 x 128, 256 threads (2 x 2 waves of 64 x 64).
+ *  SPT_TILE_256x256_4W  256 x 256, 256 threads (2 x 2 waves of 128 x 128,
+ *                    one wave per SIMD).
  */
 enum spt_tile {
     SPT_TILE_AUTO = 0,
     SPT_TILE_128x256 = 1,
     SPT_TILE_256x256 = 2,
-    SPT_TILE_128x128 = 3
+    SPT_TILE_128x128 = 3,
+    SPT_TILE_256x256_4W = 4
 };
 
 enum spt_status {

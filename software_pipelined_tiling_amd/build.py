@@ -27,30 +27,35 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-command-line-argument"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, defines=(), tag: str = "") -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-4000:]}")
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = True) -> str:
-    """Compile every source for gfx950 and link libspt.so; returns its path."""
+def build(jobs: int | None = None, verbose: bool = True, defines=(), out: str | None = None) -> str:
+    """Compile every source for gfx950 and link libspt.so (or `out`); returns its path.
+
+    `defines` are extra preprocessor definitions (tuning experiments only)."""
     os.makedirs(BUILD, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 4)
+    tag = "" if not defines else "_" + str(abs(hash(tuple(defines))))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, defines, tag), SOURCES))
+    lib = out or LIB
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr[-4000:]}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
-    return LIB
+        print(f"built {lib}", file=sys.stderr)
+    return lib
 
 
 def asm(src: str = "spt_kernels_f16.hip", out: str | None = None) -> str:

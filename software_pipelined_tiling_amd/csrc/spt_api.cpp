@@ -31,13 +31,14 @@ static const KernelTable& table_for(int dtype)
     return t[dtype];
 }
 
-const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int stages)
+const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int stages, int exact)
 {
     if (dtype < 0 || dtype > 3) return nullptr;
     const KernelTable& t = table_for(dtype);
     for (int i = 0; i < t.count; ++i) {
         const KernelEntry& e = t.entries[i];
-        if (e.bcol == bcol && e.tile == tile && e.variant == variant && e.stages == stages) return &e;
+        if (e.bcol == bcol && e.tile == tile && e.variant == variant && e.stages == stages && e.exact == exact)
+            return &e;
     }
     return nullptr;
 }
@@ -48,7 +49,7 @@ static void resolve(int& variant, int& stages, int& tile)
 {
     if (tile == 0) tile = 1;
     if (variant == V_AUTO) variant = V_DIRECT;
-    if (stages == 0) stages = variant == V_SYNC ? 1 : variant == V_REG ? 2 : (tile == 2 ? 2 : 3);
+    if (stages == 0) stages = variant == V_SYNC ? 1 : variant == V_REG ? 2 : (kTiles[tile].BKB >= 128 ? 2 : 3);
 }
 
 static bool valid_pair(int variant, int stages)
@@ -150,7 +151,11 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
         return fail(SPT_ERR_UNSUPPORTED, "operand panel exceeds 2 GiB of buffer offsets");
     if (pi.grid > INT32_MAX) return fail(SPT_ERR_UNSUPPORTED, "too many workgroups");
 
-    const KernelEntry* e = find_kernel(dtype, bcol, pi.tile_id, pi.variant, pi.stages);
+    // The exact-fit instantiation when M, N and K are multiples of the tile
+    // (same arithmetic, no tail or edge code), else the general one.
+    const bool fits = M % pi.BM == 0 && N % pi.BN == 0 && pi.k_tail == 0;
+    const KernelEntry* e = fits ? find_kernel(dtype, bcol, pi.tile_id, pi.variant, pi.stages, 1) : nullptr;
+    if (!e) e = find_kernel(dtype, bcol, pi.tile_id, pi.variant, pi.stages, 0);
     if (!e) return fail(SPT_ERR_UNSUPPORTED, "no kernel built for dtype %d layout %d tile %d variant %d stages %d",
                         dtype, b_layout, pi.tile_id, pi.variant, pi.stages);
 

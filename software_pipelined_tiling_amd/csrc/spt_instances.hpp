@@ -15,11 +15,11 @@ hipError_t launch_gemm(const GemmArgs& a, unsigned grid, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int DT, int BC, int TI, int V, int S>
+template <int DT, int BC, int TI, int V, int S, int EX = 0>
 constexpr KernelEntry entry()
 {
-    typedef Cfg<DT, BC != 0, TI, V, S> C;
-    return KernelEntry{DT, BC, TI, V, S, C::THREADS, C::LDS_BYTES, C::LOADS, &launch_gemm<C>,
+    typedef Cfg<DT, BC != 0, TI, V, S, EX != 0> C;
+    return KernelEntry{DT, BC, TI, V, S, EX, C::THREADS, C::LDS_BYTES, C::LOADS, &launch_gemm<C>,
                        (const void*)&gemm_kernel<C>};
 }
 
@@ -27,14 +27,21 @@ constexpr KernelEntry entry()
 #define SPT_PAIRS(DT, BC, TI)                                                              \
     entry<DT, BC, TI, V_SYNC, 1>(), entry<DT, BC, TI, V_REG, 1>(), entry<DT, BC, TI, V_REG, 2>(), \
         entry<DT, BC, TI, V_DIRECT, 2>()
-// The 3-stage ring where it fits in LDS (the 256 x 256 tile needs 3 x 64 KiB).
+// The 3-stage ring where it fits in LDS (the 256 x 256 tiles need 3 x 64 KiB).
 #define SPT_RING3(DT, BC, TI) entry<DT, BC, TI, V_DIRECT, 3>()
+
+// Exact-fit instantiations of the ring variants (no K tail, no edge checks).
+#define SPT_EXACT(DT, BC, TI) entry<DT, BC, TI, V_DIRECT, 2, 1>()
+#define SPT_EXACT3(DT, BC, TI) entry<DT, BC, TI, V_DIRECT, 3, 1>()
 
 #define SPT_DEFINE_TABLE(NAME, DT)                                                          \
     static const KernelEntry k_##NAME[] = {                                                \
         SPT_PAIRS(DT, 0, 1), SPT_RING3(DT, 0, 1), SPT_PAIRS(DT, 1, 1), SPT_RING3(DT, 1, 1), \
         SPT_PAIRS(DT, 0, 2), SPT_PAIRS(DT, 1, 2),                                          \
         SPT_PAIRS(DT, 0, 3), SPT_RING3(DT, 0, 3), SPT_PAIRS(DT, 1, 3), SPT_RING3(DT, 1, 3), \
+        SPT_PAIRS(DT, 0, 4), SPT_PAIRS(DT, 1, 4),                                          \
+        SPT_EXACT(DT, 0, 1), SPT_EXACT3(DT, 0, 1), SPT_EXACT(DT, 1, 1), SPT_EXACT3(DT, 1, 1), \
+        SPT_EXACT(DT, 0, 2), SPT_EXACT(DT, 1, 2), SPT_EXACT(DT, 0, 4), SPT_EXACT(DT, 1, 4), \
     };                                                                                     \
     KernelTable kernels_##NAME() { return KernelTable{k_##NAME, (int)(sizeof(k_##NAME) / sizeof(k_##NAME[0]))}; }
 

@@ -16,29 +16,48 @@
 //            register-only prefetch of Schritt 1) or S = 2 (double buffer).
 //  V_DIRECT  asynchronous global -> LDS copies (the pages' cp.async, on CDNA4
 //            buffer_load_dwordx4 ... lds, which writes LDS without a VGPR
-//            round trip) into an S-stage ring, S = 2 or 3 (sections 5, 6).
+//            round trip) into an S-stage ring, S = 2 or 3 (sections 5, 6),
+//            with a second, register-level pipeline of LDS -> VGPR fragment
+//            reads (section 7).
 //
-// Ring discipline for V_DIRECT (sections 3-5 and 9, with one ordering
-// change, see below): the prologue issues tiles 0..S-2 into stages 0..S-2.
-// Iteration t then
-//     waits until tile t's copies of this wave have landed
-//         (s_waitcnt vmcnt: at most (S-2) newer tiles' copies in flight),
-//     s_barrier                 -- every wave's copies of tile t are in LDS
-//                                  and every wave has finished reading tile
-//                                  t-1, whose stage (t+S-1) mod S is free,
-//     issues tile t+S-1 into stage (t+S-1) mod S,
-//     computes tile t from stage t mod S.
-// The pages' minimal example issues before it waits; waiting first lets a
-// single barrier serve both obligations of section 4 (never expose a stage
-// early, never release one early) and keeps S-1 tiles in flight during the
-// compute of tile t.
+// V_DIRECT schedule.  Fragments of one MFMA k-step of the wave tile sit in
+// one of two register slots.  For K tile t with KS k-steps:
+//     steps s < KS-1:  read the fragments of step s+1 into the free slot,
+//                      interleaved with the MFMAs of step s;
+//     last step:       s_waitcnt lgkmcnt(0)   -- this wave's reads of tile t
+//                                                are complete,
+//                      s_waitcnt vmcnt(n)     -- this wave's copies of tile
+//                                                t+1 have landed (n: the
+//                                                copies of younger tiles that
+//                                                may stay in flight),
+//                      s_barrier              -- every wave is past both
+//                                                waits: tile t+1 is visible
+//                                                and tile t's stage is free,
+//                      then, interleaved with the MFMAs of the last step of
+//                      tile t (whose operands are already in registers):
+//                      the copies of tile t+S into tile t's stage, and the
+//                      reads of step 0 of tile t+1 into the free slot.
+// The prologue fills all S stages (tiles past the end of K are empty copies
+// that move no memory).  The register slots act as one more
+// stage, so one barrier per K tile serves both obligations of section 4
+// (never expose a stage early, never release one early), the MFMA pipe
+// always has independent work while loads are in flight, and S tiles of
+// copies overlap the compute ("keep every level fed", section 7).
 //
-// vmcnt is this CDNA4 counterpart of cp.async.wait_group: a wave's vector
-// memory loads complete in issue order, so "at most N outstanding" is
-// "every load older than the N newest has landed" (section 3).
+// vmcnt is the CDNA4 counterpart of cp.async.wait_group (section 3): the
+// copies of one wave complete in issue order, so "at most N outstanding"
+// means "every copy older than the N newest has landed".
 //
-// A second pipeline runs inside compute(): LDS -> VGPR fragment reads of the
-// next k-step are issued before the MFMAs of the current one (section 7).
+// LDS layout.  K-contiguous tiles (A, column-major B) keep whole rows, with
+// the 16-byte chunk index XOR-swizzled by row bits so that the fragment reads
+// (ds_read_b128, 16 rows x one chunk per lane group) are bank-conflict free
+// while every 1 KiB copy still covers whole row segments (full 128-byte
+// lines when a K tile row is 128 bytes: copies of half lines run at two
+// thirds of the rate).  Row-major B is either kept as swizzled k-rows (read
+// by ds_read_b64_tr_b16 / tr_b8, full-line copies) or in "lane order": one
+// block per transposing read, holding the data in the order of the lanes that
+// read it (conflict free, half-line copies).  The producer computes which
+// global 16-byte chunk belongs at each position.
 //
 // K tails: full tiles use 16-byte copies; the last partial tile (K mod BK
 // elements) is loaded through VGPRs, and every element at k >= K is set to
@@ -58,7 +77,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
 #define SPT_LDS __attribute__((address_space(3)))
 
 // ---------------------------------------------------------------------------
@@ -72,35 +90,22 @@ __device__ __forceinline__ void wait_vmcnt()
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+// Keep the instruction order written in the source around this point.
+__device__ __forceinline__ void order_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // ---------------------------------------------------------------------------
-// LDS swizzles.  XOR of the 16-byte chunk index with bits of the row keeps
-// the fragment reads of one wave on distinct banks (checked with the LDS
-// bank-conflict counter), for both the 8-lane and the 16-lane phase of a
-// 128-bit read.
-//
-// K-contiguous tiles (A; B stored column-major): rows of NC chunks.
-template <int NC>
-__device__ __host__ constexpr int swz_k(int r)
-{
-    return NC == 4 ? (((r >> 1) ^ (r >> 3)) & 3) : NC == 8 ? ((r ^ (r >> 3)) & 7) : 0;
-}
-// N-contiguous tiles (B stored row-major): k-rows of NC chunks, read by
-// ds_read_b64_tr_b16 (ELT 2), ds_read_b64_tr_b8 (ELT 1) or ds_read_b32 (ELT 4).
-template <int ELT, int NC>
-__device__ __host__ constexpr int swz_n(int r)
-{
-    const int v = ELT == 2   ? (((r & 3) | (((r >> 3) & 1) << 2)) << 1)
-                  : ELT == 1 ? ((r & 7) | (((r >> 4) & 1) << 3))
-                             : (((r >> 2) & 3) << 2);
-    return v & (NC - 1);
-}
-
-// ---------------------------------------------------------------------------
-template <int DT_, bool BCOL_, int TILE_, int V_, int S_>
+// EXACT_: M, N and K are multiples of the tile (no K tail, no edge checks in
+// the epilogue); the dispatcher selects it only for such shapes.
+// BLANE_: row-major B kept in the lane layout (fp32 B always is).
+#ifndef SPT_B_LANE_DEFAULT
+#define SPT_B_LANE_DEFAULT false
+#endif
+template <int DT_, bool BCOL_, int TILE_, int V_, int S_, bool EXACT_ = false, bool BLANE_ = SPT_B_LANE_DEFAULT>
 struct Cfg {
     static constexpr int DT = DT_;
     static constexpr bool BCOL = BCOL_;
+    static constexpr bool EXACT = EXACT_;
+    static constexpr bool BLANE = BLANE_ || elt_bytes(DT_) == 4;
     static constexpr int TILE = TILE_, V = V_, S = S_;
     static constexpr int BM = kTiles[TILE_].BM, BN = kTiles[TILE_].BN;
     static constexpr int ELT = elt_bytes(DT_);
@@ -111,9 +116,8 @@ struct Cfg {
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;  // wave tile
     static constexpr int FM = WTM / 16, FN = WTN / 16;             // 16x16 MFMA tiles per wave
     static constexpr int KSTEP = 4 * CE;  // k per MFMA step: 4 lane groups x one 16-byte chunk
-    static constexpr int KSTEPS = BK / KSTEP;
-    static constexpr int NCA = kTiles[TILE_].BKB / 16;  // chunks per row of A (and of B col-major)
-    static constexpr int NCBR = BN * ELT / 16;          // chunks per k-row of B row-major
+    static constexpr int KS = BK / KSTEP;  // MFMA k-steps per K tile
+    static constexpr int MB = BM / 16, NB = BN / 16;  // 16-row / 16-column blocks
     static constexpr int A_BYTES = BM * BK * ELT;
     static constexpr int B_BYTES = BK * BN * ELT;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
@@ -121,16 +125,18 @@ struct Cfg {
     static constexpr int A_CPT = A_BYTES / 16 / THREADS;  // 16-byte copies per thread per stage
     static constexpr int B_CPT = B_BYTES / 16 / THREADS;
     static constexpr int LOADS = A_CPT + B_CPT;            // vmcnt units per tile per thread
+    // 16x16 wave tiles of 128 x 128 need the whole register file: one wave per SIMD
+    static constexpr int WAVES_PER_SIMD = FM * FN > 32 ? 1 : 2;
 
     static_assert(BK % KSTEP == 0, "BK must hold whole MFMA steps");
-    static_assert(A_BYTES % (16 * THREADS) == 0 && B_BYTES % (16 * THREADS) == 0,
-                  "a stage must split into whole 16-byte copies per thread");
+    static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0,
+                  "a stage must split into whole 1 KiB copies per wave");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must hold whole 16x16 MFMA tiles");
     static_assert(LDS_BYTES <= kLdsPerCu, "LDS ring exceeds 160 KiB");
     static_assert(V_ != V_SYNC || S_ == 1, "SYNC has one stage");
     static_assert(V_ != V_REG || (S_ == 1 || S_ == 2), "REG has 1 or 2 stages");
     static_assert(V_ != V_DIRECT || (S_ == 2 || S_ == 3), "DIRECT has 2 or 3 stages");
-    static_assert((S_ >= 2 ? (S_ - 2) * LOADS : 0) < 64, "vmcnt range");
+    static_assert((S_ - 1) * LOADS < 64, "vmcnt range");
 };
 
 template <int DT>
@@ -157,9 +163,8 @@ __device__ __forceinline__ void mma(typename AccT<DT>::type& acc, i32x4_t x, i32
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(x, y, acc, 0, 0, 0);
     } else {
         // fp32: a chunk holds 4 consecutive k per lane group; MFMA j takes element j,
-        // so lane group g supplies k = 4g + j to both operands.
-        // (whole-vector bit casts: a bit cast of one vector element is not used, it
-        // does not honour the element index)
+        // so lane group g supplies k = 4g + j to both operands.  (Whole-vector bit
+        // casts: a bit cast of one vector element does not honour the index.)
         const f32x4_t xf = __builtin_bit_cast(f32x4_t, x), yf = __builtin_bit_cast(f32x4_t, y);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xf[j], yf[j], acc, 0, 0, 0);
@@ -186,8 +191,8 @@ __device__ __forceinline__ i32x4_t rsrc_words(const char* base, uint32_t bytes)
 // `lds` must be wave-uniform.  Written as inline asm so that the compiler
 // does not guard later LDS reads with waits of its own (it cannot tell the
 // ring stages apart and would drain every copy in flight); the ring's
-// s_waitcnt vmcnt + s_barrier placement is the only synchronisation.  The
-// s_nop covers the M0-write -> LDS-DMA hazard.
+// s_waitcnt vmcnt + s_barrier placement is the only synchronisation.  M0
+// carries the LDS address; the s_nop covers the M0-write -> LDS-DMA hazard.
 __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t lds, int voffset)
 {
     asm volatile(
@@ -215,55 +220,174 @@ __device__ __forceinline__ i32x4_t keep_bytes(i32x4_t v, int valid)
 template <class C>
 struct Gemm {
     typedef typename AccT<C::DT>::type acc_t;
+    typedef i32x4_t Slot[C::FM + C::FN];  // one k-step of A (FM) and B (FN) fragments
 
-    // Per-thread copy geometry (loop invariant).
-    struct Copy {
-        int a_voff[C::A_CPT];  // byte offset of this thread's A chunks from the tile base
-        int b_voff[C::B_CPT];
-    };
-    // Per-lane LDS fragment offsets within one stage (loop invariant).
-    struct Frag {
-        int a[C::FM][C::KSTEPS];
-        int b[C::FN][C::BCOL ? C::KSTEPS : 1];
-    };
-
-    // A chunk q of a stage sits at LDS byte 16q; it holds logical chunk c of row r.
-    static __device__ __forceinline__ void a_chunk(int q, int& r, int& c)
+    // ---- LDS layout --------------------------------------------------------
+    // K-contiguous tiles (A; column-major B): rows of RK = BK * ELT bytes
+    // (NCK 16-byte chunks), chunk c of row r at chunk position c ^ swz_k(r).
+    // Rows stay whole in LDS, so one 1 KiB copy covers 1024 / RK full row
+    // segments; the XOR keeps the fragment reads (16 rows x one chunk) free of
+    // bank conflicts on gfx950 (measured with the LDS bank-conflict counter).
+    static constexpr int RK = C::BK * C::ELT, NCK = RK / 16;
+    static_assert(NCK == 4 || NCK == 8, "K-contiguous rows of 64 or 128 bytes");
+    static __device__ __forceinline__ constexpr int swz_k(int r) { return (r >> 1) & (NCK - 1); }
+    // Row-major B, row layout: k-rows of RN = BN * ELT bytes (NCN chunks), chunk
+    // c of k-row r at c ^ swz_n(r); read by ds_read_b64_tr_b16 / tr_b8.
+    static constexpr int RN = C::BN * C::ELT, NCN = RN / 16;
+    static __device__ __forceinline__ constexpr int swz_n(int r) { return C::ELT == 2 ? ((r & 3) << 1) : (r & 7); }
+    // Row-major B, lane layout: block (nb, s, h) of 64 lanes x (8 | 8 | 4) bytes
+    // in the order of the lanes of one ds_read_b64_tr_b16 / tr_b8 / ds_read_b32.
+    static constexpr int BR_BLOCK = C::ELT == 4 ? 256 : 512;
+    static constexpr int BR_SUB = C::ELT == 4 ? 4 : 2;  // blocks per (nb, s)
+    static constexpr int br_block(int nb, int s, int h)
     {
-        r = q / C::NCA;
-        c = (q % C::NCA) ^ swz_k<C::NCA>(r);
+        return C::A_BYTES + ((s * BR_SUB + h) * C::NB + nb) * BR_BLOCK;
     }
-    static __device__ __forceinline__ void b_chunk(int q, int& r, int& c)
+
+    // Stage chunk q of the A region -> (row, k) of the tile it holds.
+    static __device__ __forceinline__ void a_src(int q, int& row, int& k)
+    {
+        row = q / NCK;
+        k = ((q % NCK) ^ swz_k(row)) * C::CE;
+    }
+    // Stage chunk q of the B region -> (k, n) of the tile it holds.
+    static __device__ __forceinline__ void b_src(int q, int& k, int& n)
     {
         if constexpr (C::BCOL) {
-            r = q / C::NCA;
-            c = (q % C::NCA) ^ swz_k<C::NCA>(r);
+            n = q / NCK;
+            k = ((q % NCK) ^ swz_k(n)) * C::CE;
+        } else if constexpr (!C::BLANE) {
+            k = q / NCN;
+            n = ((q % NCN) ^ swz_n(k)) * C::CE;
+        } else if constexpr (C::ELT == 2) {
+            // lane l = 16 g + i of a tr_b16 read gets k-rows 8g + 4h + (i >> 2) ... at columns
+            // 4 (i & 3) .. + 3; a 16-byte chunk c holds lanes 2c, 2c + 1.
+            const int blk = q >> 5, c = q & 31;
+            const int nb = blk % C::NB, sh = blk / C::NB;
+            const int s = sh >> 1, h = sh & 1;
+            k = s * C::KSTEP + 8 * (c >> 3) + 4 * h + ((c & 7) >> 1);
+            n = 16 * nb + 8 * (c & 1);
+        } else if constexpr (C::ELT == 1) {
+            // tr_b8: lane 16 g + i gets k-rows 16 g + 8 h + (i >> 1) at columns 8 (i & 1) .. + 7.
+            const int blk = q >> 5, c = q & 31;
+            const int nb = blk % C::NB, sh = blk / C::NB;
+            const int s = sh >> 1, h = sh & 1;
+            k = s * C::KSTEP + 16 * (c >> 3) + 8 * h + (c & 7);
+            n = 16 * nb;
         } else {
-            r = q / C::NCBR;
-            c = (q % C::NCBR) ^ swz_n<C::ELT, C::NCBR>(r);
+            // fp32, ds_read_b32 t: lane 16 g + j gets k-row 4 g + t at column j.
+            const int blk = q >> 4, c = q & 15;
+            const int nb = blk % C::NB, st = blk / C::NB;
+            const int s = st >> 2, t = st & 3;
+            k = s * C::KSTEP + 4 * (c >> 2) + t;
+            n = 16 * nb + 4 * (c & 3);
         }
     }
+
+    // ---- fragment reads ---------------------------------------------------------
+    // Per-lane LDS byte offsets of this wave's fragments within a stage, for
+    // MFMA row 0 / column 0 of the wave tile; other rows / columns add an
+    // immediate.  A fragment (m, s): 16 rows x the 16-byte chunk 4s + g.
+    static constexpr int B_OFFS = C::BCOL ? C::KS : (C::BLANE ? 1 : C::FN);
+    struct Lanes {
+        int a[C::KS];
+        int b[B_OFFS];
+    };
+    static __device__ void setup_lanes(int lane, int mb0, int nb0, Lanes& L)
+    {
+        const int g = lane >> 4, l16 = lane & 15;
+        // swz_k(16 mb + l16) == swz_k(l16): the row-block index never reaches the XOR bits
+#pragma unroll
+        for (int s = 0; s < C::KS; ++s) {
+            L.a[s] = (16 * mb0 + l16) * RK + 16 * ((4 * s + g) ^ swz_k(l16));
+            if constexpr (C::BCOL) L.b[s] = C::A_BYTES + (16 * nb0 + l16) * RK + 16 * ((4 * s + g) ^ swz_k(l16));
+        }
+        if constexpr (!C::BCOL && C::BLANE) {
+            L.b[0] = br_block(nb0, 0, 0) + lane * (C::ELT == 4 ? 4 : 8);
+        } else if constexpr (!C::BCOL && C::ELT == 2) {
+            // tr_b16: lane (g, i) fetches k-row 8g + (i >> 2) (+ 4h + KSTEP s) at columns
+            // 4 (i & 3) .. + 3 of column block nb; swz_n only sees k-row bits 0, 1.
+#pragma unroll
+            for (int n = 0; n < C::FN; ++n) {
+                const int kr = 8 * g + (l16 >> 2);
+                const int c = 2 * (nb0 + n) + ((l16 & 3) >> 1);
+                L.b[n] = C::A_BYTES + kr * RN + 16 * (c ^ swz_n(kr)) + 8 * (l16 & 1);
+            }
+        } else if constexpr (!C::BCOL && C::ELT == 1) {
+            // tr_b8: lane (g, i) fetches k-row 16g + (i >> 1) (+ 8h + KSTEP s) at columns
+            // 8 (i & 1) .. + 7 of column block nb; swz_n only sees k-row bits 0..2.
+#pragma unroll
+            for (int n = 0; n < C::FN; ++n) {
+                const int kr = 16 * g + (l16 >> 1);
+                L.b[n] = C::A_BYTES + kr * RN + 16 * ((nb0 + n) ^ swz_n(kr)) + 8 * (l16 & 1);
+            }
+        }
+    }
+
+    static __device__ __forceinline__ i32x4_t read_a(const SPT_LDS char* st, const Lanes& L, int m, int s)
+    {
+        return *(const SPT_LDS i32x4_t*)(st + L.a[s] + 16 * m * RK);
+    }
+    static __device__ __forceinline__ i32x4_t read_b(const SPT_LDS char* st, const Lanes& L, int n, int s)
+    {
+        if constexpr (C::BCOL) {
+            return *(const SPT_LDS i32x4_t*)(st + L.b[s] + 16 * n * RK);
+        } else if constexpr (C::ELT == 4) {  // lane layout only
+            i32x4_t v;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                v[t] = *(const SPT_LDS int*)(st + L.b[0] + (br_block(n, s, t) - C::A_BYTES));
+            return v;
+        } else {
+            int o0, o1;  // the two transposing reads (k-rows +0.. and +4 / +8 ..)
+            if constexpr (C::BLANE) {
+                o0 = L.b[0] + (br_block(n, s, 0) - C::A_BYTES);
+                o1 = L.b[0] + (br_block(n, s, 1) - C::A_BYTES);
+            } else {
+                o0 = L.b[n] + s * C::KSTEP * RN;
+                o1 = o0 + (C::ELT == 2 ? 4 : 8) * RN;
+            }
+            if constexpr (C::ELT == 2) {
+                typedef __fp16 fp16x4_raw __attribute__((__vector_size__(4 * sizeof(__fp16))));
+                const fp16x4_raw lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((SPT_LDS fp16x4_raw*)(st + o0));
+                const fp16x4_raw hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((SPT_LDS fp16x4_raw*)(st + o1));
+                const i32x2_t l2 = __builtin_bit_cast(i32x2_t, lo), h2 = __builtin_bit_cast(i32x2_t, hi);
+                return (i32x4_t){l2.x, l2.y, h2.x, h2.y};
+            } else {
+                const i32x2_t lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SPT_LDS i32x2_t*)(st + o0));
+                const i32x2_t hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SPT_LDS i32x2_t*)(st + o1));
+                return (i32x4_t){lo.x, lo.y, hi.x, hi.y};
+            }
+        }
+    }
+
+    // Per-thread copy geometry (loop invariant): byte offsets of this thread's
+    // A and B chunks from the K tile's base.
+    struct Copy {
+        int a_voff[C::A_CPT];
+        int b_voff[C::B_CPT];
+    };
 
     static __device__ void setup_copy(const GemmArgs& p, int m0, int n0, int tid, Copy& cp)
     {
         const int rows_a = min(C::BM, p.M - m0);
 #pragma unroll
         for (int i = 0; i < C::A_CPT; ++i) {
-            int r, c;
-            a_chunk(i * C::THREADS + tid, r, c);
+            int r, k;
+            a_src(i * C::THREADS + tid, r, k);
             r = min(r, rows_a - 1);  // M edge: any in-range row (its outputs are not stored)
-            cp.a_voff[i] = r * p.lda * C::ELT + c * 16;
+            cp.a_voff[i] = r * p.lda * C::ELT + k * C::ELT;
         }
 #pragma unroll
         for (int i = 0; i < C::B_CPT; ++i) {
-            int r, c;
-            b_chunk(i * C::THREADS + tid, r, c);
+            int k, n;
+            b_src(i * C::THREADS + tid, k, n);
             if constexpr (C::BCOL) {
-                r = min(r, min(C::BN, p.N - n0) - 1);  // N edge
-                cp.b_voff[i] = r * p.ldb * C::ELT + c * 16;
+                n = min(n, min(C::BN, p.N - n0) - 1);  // N edge
+                cp.b_voff[i] = n * p.ldb * C::ELT + k * C::ELT;
             } else {
-                if (n0 + c * C::CE >= p.N) c = 0;  // N edge: any in-range chunk
-                cp.b_voff[i] = r * p.ldb * C::ELT + c * 16;
+                if (n0 + n >= p.N) n = 0;  // N edge: any in-range chunk
+                cp.b_voff[i] = k * p.ldb * C::ELT + n * C::ELT;
             }
         }
     }
@@ -293,63 +417,58 @@ struct Gemm {
             bytes = (uint32_t)min64((rows * p.ldb - n0) * C::ELT, 0x7ffffff0ll);
         }
     }
-    static __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_a(const GemmArgs& p, int m0, int t)
+
+    // ---- V_DIRECT producer ---------------------------------------------------
+    // Copy j (0 .. LOADS-1) of K tile t into the stage at LDS byte `st`: the
+    // copies of wave w, number i of an operand cover that operand's stage
+    // chunks [(i WAVES + w) 64, + 64).
+    struct Dma {
+        i32x4_t ra, rb;
+        uint32_t st;
+    };
+    static __device__ __forceinline__ Dma dma_begin(const GemmArgs& p, int m0, int n0, int t, uint32_t st)
     {
-        const char* b;
-        uint32_t n;
-        span_a(p, m0, t, b, n);
-        return make_rsrc(b, n);
+        const char *pa, *pb;
+        uint32_t na, nb;
+        const int tt = t < p.k_full ? t : 0;  // beyond the last full tile: an empty copy
+        span_a(p, m0, tt, pa, na);
+        span_b(p, n0, tt, pb, nb);
+        if (t >= p.k_full) na = nb = 0;
+        return Dma{rsrc_words(pa, na), rsrc_words(pb, nb), st};
     }
-    static __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_b(const GemmArgs& p, int n0, int t)
+    static __device__ __forceinline__ void dma_issue(const Dma& d, int j, int wave, const Copy& cp)
     {
-        const char* b;
-        uint32_t n;
-        span_b(p, n0, t, b, n);
-        return make_rsrc(b, n);
+        if (j < C::A_CPT)
+            dma16(d.ra, d.st + (j * C::WAVES + wave) * 1024, cp.a_voff[j]);
+        else
+            dma16(d.rb, d.st + C::A_BYTES + ((j - C::A_CPT) * C::WAVES + wave) * 1024,
+                  cp.b_voff[j - C::A_CPT]);
     }
 
-    // V_DIRECT producer: issue all copies of tile t into the stage at `st`.
-    // Each buffer_load ... lds writes 64 x 16 contiguous bytes at M0, so the
-    // copies of wave w, instruction i cover stage chunks [i*THREADS + 64w, +64).
-    static __device__ __forceinline__ void issue_direct(const GemmArgs& p, int m0, int n0, int t,
-                                                        SPT_LDS char* st, int wave, const Copy& cp)
+    // ---- V_REG / V_SYNC producer: global -> VGPR -> LDS ------------------------
+    static __device__ __forceinline__ void load_regs(const GemmArgs& p, int m0, int n0, int t,
+                                                     const Copy& cp, i32x4_t (&ra_)[C::A_CPT],
+                                                     i32x4_t (&rb_)[C::B_CPT])
     {
         const char *pa, *pb;
         uint32_t na, nb;
         span_a(p, m0, t, pa, na);
         span_b(p, n0, t, pb, nb);
-        const i32x4_t ra = rsrc_words(pa, na);
-        const i32x4_t rb = rsrc_words(pb, nb);
-        const uint32_t base = (uint32_t)(uintptr_t)st;
-#pragma unroll
-        for (int i = 0; i < C::A_CPT; ++i)
-            dma16(ra, base + (i * C::THREADS + wave * 64) * 16, cp.a_voff[i]);
-#pragma unroll
-        for (int i = 0; i < C::B_CPT; ++i)
-            dma16(rb, base + C::A_BYTES + (i * C::THREADS + wave * 64) * 16, cp.b_voff[i]);
-    }
-
-    // V_REG / V_SYNC producer, part 1: global -> VGPR.
-    static __device__ __forceinline__ void load_regs(const GemmArgs& p, int m0, int n0, int t,
-                                                     const Copy& cp, i32x4_t (&ra_)[C::A_CPT],
-                                                     i32x4_t (&rb_)[C::B_CPT])
-    {
-        const __amdgpu_buffer_rsrc_t ra = rsrc_a(p, m0, t);
-        const __amdgpu_buffer_rsrc_t rb = rsrc_b(p, n0, t);
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(pa, na), rb = make_rsrc(pb, nb);
 #pragma unroll
         for (int i = 0; i < C::A_CPT; ++i) ra_[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, cp.a_voff[i], 0, 0);
 #pragma unroll
         for (int i = 0; i < C::B_CPT; ++i) rb_[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, cp.b_voff[i], 0, 0);
     }
 
-    // Producer, part 2: VGPR -> LDS (ds_write_b128 at the chunk's stage position).
+    // Thread tid's copies sit at the same stage chunks as in the V_DIRECT copies
+    // (chunk i THREADS + tid), written with ds_write_b128.
     static __device__ __forceinline__ void store_regs(SPT_LDS char* st, int tid,
                                                       const i32x4_t (&ra_)[C::A_CPT],
                                                       const i32x4_t (&rb_)[C::B_CPT])
     {
 #pragma unroll
-        for (int i = 0; i < C::A_CPT; ++i)
-            *(SPT_LDS i32x4_t*)(st + (i * C::THREADS + tid) * 16) = ra_[i];
+        for (int i = 0; i < C::A_CPT; ++i) *(SPT_LDS i32x4_t*)(st + (i * C::THREADS + tid) * 16) = ra_[i];
 #pragma unroll
         for (int i = 0; i < C::B_CPT; ++i)
             *(SPT_LDS i32x4_t*)(st + C::A_BYTES + (i * C::THREADS + tid) * 16) = rb_[i];
@@ -362,140 +481,136 @@ struct Gemm {
     {
         const int t = p.k_full;
         const int kt = p.k_tail;  // valid k inside the tile: [0, kt)
-        const __amdgpu_buffer_rsrc_t ra = rsrc_a(p, m0, t);
-        const __amdgpu_buffer_rsrc_t rb = rsrc_b(p, n0, t);
+        const char *pa, *pb;
+        uint32_t na, nb;
+        span_a(p, m0, t, pa, na);
+        span_b(p, n0, t, pb, nb);
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(pa, na), rb = make_rsrc(pb, nb);
         const int rows_a = min(C::BM, p.M - m0);
 #pragma unroll
         for (int i = 0; i < C::A_CPT; ++i) {
-            int r, c;
-            a_chunk(i * C::THREADS + tid, r, c);
+            int r, k;
+            a_src(i * C::THREADS + tid, r, k);
             r = min(r, rows_a - 1);
-            const int valid = kt - c * C::CE;  // elements of this chunk below K
-            const int voff = r * p.lda * C::ELT + (valid > 0 ? c * 16 : 0);
+            const int valid = kt - k;  // elements of this chunk below K
+            const int voff = r * p.lda * C::ELT + (valid > 0 ? k * C::ELT : 0);
             ra_[i] = keep_bytes(__builtin_amdgcn_raw_buffer_load_b128(ra, voff, 0, 0), valid * C::ELT);
         }
 #pragma unroll
         for (int i = 0; i < C::B_CPT; ++i) {
-            int r, c;
-            b_chunk(i * C::THREADS + tid, r, c);
+            int k, n;
+            b_src(i * C::THREADS + tid, k, n);
             if constexpr (C::BCOL) {
-                r = min(r, min(C::BN, p.N - n0) - 1);
-                const int valid = kt - c * C::CE;
-                const int voff = r * p.ldb * C::ELT + (valid > 0 ? c * 16 : 0);
+                n = min(n, min(C::BN, p.N - n0) - 1);
+                const int valid = kt - k;
+                const int voff = n * p.ldb * C::ELT + (valid > 0 ? k * C::ELT : 0);
                 rb_[i] = keep_bytes(__builtin_amdgcn_raw_buffer_load_b128(rb, voff, 0, 0), valid * C::ELT);
             } else {
-                if (n0 + c * C::CE >= p.N) c = 0;
-                const bool ok = r < kt;  // k-row of this chunk below K
-                const int voff = (ok ? r : 0) * p.ldb * C::ELT + c * 16;
+                if (n0 + n >= p.N) n = 0;
+                const bool ok = k < kt;  // k-row of this chunk below K
+                const int voff = (ok ? k : 0) * p.ldb * C::ELT + n * C::ELT;
                 rb_[i] = keep_bytes(__builtin_amdgcn_raw_buffer_load_b128(rb, voff, 0, 0), ok ? 16 : 0);
             }
         }
     }
 
-    static __device__ void setup_frag(int wm0, int wn0, int lane, Frag& f)
+    // ---- consumer ----------------------------------------------------------------
+    // Fragment read j (0 .. FM+FN-1) of k-step s into `slot`.
+    static __device__ __forceinline__ void read_frag(const SPT_LDS char* st, const Lanes& L, int s, int j,
+                                                     Slot& slot)
     {
-        const int l16 = lane & 15, g = lane >> 4;
+        if (j < C::FM)
+            slot[j] = read_a(st, L, j, s);
+        else
+            slot[j] = read_b(st, L, j - C::FM, s);
+    }
+    static __device__ __forceinline__ void read_slot(const SPT_LDS char* st, const Lanes& L, int s, Slot& slot)
+    {
 #pragma unroll
-        for (int m = 0; m < C::FM; ++m)
+        for (int j = 0; j < C::FM + C::FN; ++j) read_frag(st, L, s, j, slot);
+    }
+    static __device__ __forceinline__ void mma_one(const Slot& slot, int j, acc_t (&acc)[C::FM][C::FN])
+    {
+        const int m = j / C::FN, n = j % C::FN;
+        mma<C::DT>(acc[m][n], slot[C::FM + n], slot[m]);
+    }
+
+    // Slot in the MFMA sequence of one k-step after which the A fragment of row
+    // ma of the next step is read: once row ma has used the old one (so its
+    // registers are reused) and after the `lead` copies and FN B reads.
+    static constexpr int a_read_at(int ma, int lead)
+    {
+        return (ma * C::FN + C::FN - 1) > (lead + C::FN + ma) ? (ma * C::FN + C::FN - 1) : (lead + C::FN + ma);
+    }
+
+    // The FM x FN MFMAs of one k-step from `use`, row by row, with side work
+    // beside them in this order: NDMA copies (j < NDMA), then the FN B fragments
+    // of step `snext` of stage `src` into `nxt`, then its A fragments as rows
+    // free up (READ).  Every side instruction sits after one MFMA; a fence keeps
+    // the written order.
+    template <int NDMA, bool READ>
+    static __device__ __forceinline__ void step(const Slot& use, Slot& nxt, const SPT_LDS char* src, int snext,
+                                                const Lanes& L, const Dma& d, int wave, const Copy& cp,
+                                                acc_t (&acc)[C::FM][C::FN])
+    {
+        constexpr int NJ = C::FM * C::FN;
 #pragma unroll
-            for (int s = 0; s < C::KSTEPS; ++s) {
-                const int r = wm0 + 16 * m + l16;
-                const int c = 4 * s + g;
-                f.a[m][s] = r * C::NCA * 16 + ((c ^ swz_k<C::NCA>(r)) * 16);
+        for (int j = 0; j < NJ; ++j) {
+            mma_one(use, j, acc);
+            if (j < NDMA) dma_issue(d, j, wave, cp);
+            if (READ) {
+                const int nb = j - NDMA;
+                if (nb >= 0 && nb < C::FN) read_frag(src, L, snext, C::FM + nb, nxt);
+#pragma unroll
+                for (int ma = 0; ma < C::FM; ++ma)
+                    if (a_read_at(ma, NDMA) == j) read_frag(src, L, snext, ma, nxt);
             }
+            order_fence();
+        }
+        // side work whose slot fell beyond the last MFMA
 #pragma unroll
-        for (int n = 0; n < C::FN; ++n) {
-            if constexpr (C::BCOL) {
+        for (int j = NJ; j < NDMA; ++j) dma_issue(d, j, wave, cp);
+        if (READ) {
 #pragma unroll
-                for (int s = 0; s < C::KSTEPS; ++s) {
-                    const int r = wn0 + 16 * n + l16;
-                    const int c = 4 * s + g;
-                    f.b[n][s] = C::A_BYTES + r * C::NCA * 16 + ((c ^ swz_k<C::NCA>(r)) * 16);
-                }
-            } else if constexpr (C::ELT == 2) {
-                // ds_read_b64_tr_b16: in each 16-lane group, lane i fetches 4 elements of
-                // k-row (i / 4) at columns 4*(i % 4) .. +3; afterwards lane j holds the 4
-                // k-rows of column j.  Offsets for (s, h) = (0, 0); the swizzle does not
-                // depend on the k-row bits that s and h add.
-                const int kr = 8 * g + (l16 >> 2);
-                const int col = wn0 + 16 * n + 4 * (l16 & 3);
-                const int c = col / 8;
-                f.b[n][0] = C::A_BYTES + kr * C::NCBR * 16 + ((c ^ swz_n<2, C::NCBR>(kr)) * 16) +
-                            (col % 8) * 2;
-            } else if constexpr (C::ELT == 1) {
-                // ds_read_b64_tr_b8: lane i fetches 8 bytes of k-row (i / 2) at columns
-                // 8*(i % 2) .. +7; afterwards lane j holds 8 k-rows of column j.
-                const int kr = 16 * g + (l16 >> 1);
-                const int col = wn0 + 16 * n + 8 * (l16 & 1);
-                const int c = col / 16;
-                f.b[n][0] = C::A_BYTES + kr * C::NCBR * 16 + ((c ^ swz_n<1, C::NCBR>(kr)) * 16) +
-                            (col % 16);
-            } else {
-                // fp32, ds_read_b32: lane (g, j) reads k-row 4g + j' for MFMA j'.
-                const int kr = 4 * g;
-                const int col = wn0 + 16 * n + l16;
-                const int c = col / 4;
-                f.b[n][0] = C::A_BYTES + kr * C::NCBR * 16 + ((c ^ swz_n<4, C::NCBR>(kr)) * 16) +
-                            (col % 4) * 4;
-            }
+            for (int nb = 0; nb < C::FN; ++nb)
+                if (nb + NDMA >= NJ) read_frag(src, L, snext, C::FM + nb, nxt);
+#pragma unroll
+            for (int ma = 0; ma < C::FM; ++ma)
+                if (a_read_at(ma, NDMA) >= NJ) read_frag(src, L, snext, ma, nxt);
         }
     }
 
-    static __device__ __forceinline__ i32x4_t read_a(const SPT_LDS char* st, const Frag& f, int m, int s)
+    // One stage, all k-steps (REG / SYNC / the K tail): the fragments of step
+    // s+1 are read beside the MFMAs of step s.
+    static __device__ __forceinline__ void compute(const SPT_LDS char* st, const Lanes& L, int wave,
+                                                   const Copy& cp, acc_t (&acc)[C::FM][C::FN])
     {
-        return *(const SPT_LDS i32x4_t*)(st + f.a[m][s]);
-    }
-    static __device__ __forceinline__ i32x4_t read_b(const SPT_LDS char* st, const Frag& f, int n, int s)
-    {
-        if constexpr (C::BCOL) {
-            return *(const SPT_LDS i32x4_t*)(st + f.b[n][s]);
-        } else if constexpr (C::ELT == 2) {
-            typedef __fp16 fp16x4_raw __attribute__((__vector_size__(4 * sizeof(__fp16))));
-            const SPT_LDS char* b = st + f.b[n][0] + s * C::KSTEP * C::NCBR * 16;
-            const fp16x4_raw lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((SPT_LDS fp16x4_raw*)b);
-            const fp16x4_raw hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4f16((SPT_LDS fp16x4_raw*)(b + 4 * C::NCBR * 16));
-            const i32x2_t l2 = __builtin_bit_cast(i32x2_t, lo), h2 = __builtin_bit_cast(i32x2_t, hi);
-            return (i32x4_t){l2.x, l2.y, h2.x, h2.y};
-        } else if constexpr (C::ELT == 1) {
-            const SPT_LDS char* b = st + f.b[n][0] + s * C::KSTEP * C::NCBR * 16;
-            const i32x2_t lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SPT_LDS i32x2_t*)b);
-            const i32x2_t hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SPT_LDS i32x2_t*)(b + 8 * C::NCBR * 16));
-            return (i32x4_t){lo.x, lo.y, hi.x, hi.y};
-        } else {
-            const SPT_LDS char* b = st + f.b[n][0] + s * C::KSTEP * C::NCBR * 16;
-            i32x4_t v;
+        Slot sl[2];
+        read_slot(st, L, 0, sl[0]);
+        const Dma none{};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = *(const SPT_LDS int*)(b + j * C::NCBR * 16);
-            return v;
+        for (int s = 0; s < C::KS; ++s) {
+            if (s + 1 < C::KS)
+                step<0, true>(sl[s & 1], sl[(s + 1) & 1], st, s + 1, L, none, wave, cp, acc);
+            else
+                step<0, false>(sl[s & 1], sl[(s + 1) & 1], st, 0, L, none, wave, cp, acc);
         }
     }
 
-    // Consume one stage: KSTEPS MFMA steps over the FM x FN tiles of this wave.
-    // Register double buffer: the fragments of step s+1 are read before the
-    // MFMAs of step s are issued.
-    static __device__ __forceinline__ void compute(const SPT_LDS char* st, const Frag& f,
-                                                   acc_t (&acc)[C::FM][C::FN])
+    // Wait until at most n (0 .. S-1) younger tiles' copies are in flight.
+    static __device__ __forceinline__ void wait_tiles(int n)
     {
-        i32x4_t af[2][C::FM], bf[2][C::FN];
-#pragma unroll
-        for (int m = 0; m < C::FM; ++m) af[0][m] = read_a(st, f, m, 0);
-#pragma unroll
-        for (int n = 0; n < C::FN; ++n) bf[0][n] = read_b(st, f, n, 0);
-#pragma unroll
-        for (int s = 0; s < C::KSTEPS; ++s) {
-            const int cur = s & 1, nxt = cur ^ 1;
-            if (s + 1 < C::KSTEPS) {
-#pragma unroll
-                for (int m = 0; m < C::FM; ++m) af[nxt][m] = read_a(st, f, m, s + 1);
-#pragma unroll
-                for (int n = 0; n < C::FN; ++n) bf[nxt][n] = read_b(st, f, n, s + 1);
+        if constexpr (C::S >= 3) {
+            if (n >= 2) {
+                wait_vmcnt<2 * C::LOADS>();
+                return;
             }
-#pragma unroll
-            for (int m = 0; m < C::FM; ++m)
-#pragma unroll
-                for (int n = 0; n < C::FN; ++n) mma<C::DT>(acc[m][n], bf[cur][n], af[cur][m]);
         }
+        if (n >= 1) {
+            wait_vmcnt<C::LOADS>();
+            return;
+        }
+        wait_vmcnt<0>();
     }
 
     // XCD-aware placement.  Workgroups are dispatched round-robin over the 8
@@ -521,6 +636,15 @@ struct Gemm {
                                    const acc_t (&acc)[C::FM][C::FN])
     {
         const int l16 = lane & 15, g = lane >> 4;
+        if (C::EXACT || (m0 + C::BM <= p.M && n0 + C::BN <= p.N)) {  // whole tile inside C
+            char* base = p.C + ((long long)(m0 + wm0 + l16) * p.ldc + n0 + wn0 + 4 * g) * 4;
+#pragma unroll
+            for (int m = 0; m < C::FM; ++m)
+#pragma unroll
+                for (int n = 0; n < C::FN; ++n)
+                    *(acc_t*)(base + ((long long)16 * m * p.ldc + 16 * n) * 4) = acc[m][n];
+            return;
+        }
 #pragma unroll
         for (int m = 0; m < C::FM; ++m) {
             const int row = m0 + wm0 + 16 * m + l16;
@@ -541,6 +665,78 @@ struct Gemm {
         }
     }
 
+    // V_DIRECT main loop (see the schedule at the top of this file).  Every
+    // iteration is the same: past the last K tile the ring issues empty copies
+    // (a zero-length buffer range moves no memory, lanes read as out of range),
+    // as "Hiding Memory Latency ...", section 8, turns out-of-range tiles into
+    // zero-filled stages, so the vmcnt count per tile never changes and the
+    // loop body has no branches.  The last tile's reads of "tile nf" are
+    // discarded; the ring is drained before the kernel leaves it.
+    static __device__ __forceinline__ void loop_direct(const GemmArgs& p, int m0, int n0, int wave,
+                                                       const Lanes& L, SPT_LDS char* smem, const Copy& cp,
+                                                       acc_t (&acc)[C::FM][C::FN])
+    {
+        const int nf = p.k_full;
+        if (nf == 0) return;
+        const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+        // prologue: tiles 0 .. S-1 into stages 0 .. S-1
+#pragma unroll
+        for (int i = 0; i < C::S; ++i) {
+            const Dma d = dma_begin(p, m0, n0, i, lds0 + i * C::STAGE_BYTES);
+#pragma unroll
+            for (int j = 0; j < C::LOADS; ++j) dma_issue(d, j, wave, cp);
+        }
+        wait_vmcnt<(C::S - 1) * C::LOADS>();  // tile 0 landed
+        barrier();
+        Slot sl[2];
+        read_slot(smem, L, 0, sl[0]);
+
+        int t = 0, rs = 0;  // tile, and the stage it sits in
+        if constexpr (C::KS % 2 == 0) {
+            for (; t < nf; ++t) {
+                tile_direct<0>(p, m0, n0, t, rs, wave, L, smem, cp, sl, acc);
+                rs = rs + 1 == C::S ? 0 : rs + 1;
+            }
+        } else {
+            // an odd number of k-steps flips the register slot of step 0 every tile:
+            // tiles go in pairs so the slot stays a compile-time constant
+            for (; t + 1 < nf; t += 2) {
+                tile_direct<0>(p, m0, n0, t, rs, wave, L, smem, cp, sl, acc);
+                rs = rs + 1 == C::S ? 0 : rs + 1;
+                tile_direct<1>(p, m0, n0, t + 1, rs, wave, L, smem, cp, sl, acc);
+                rs = rs + 1 == C::S ? 0 : rs + 1;
+            }
+            if (t < nf) tile_direct<0>(p, m0, n0, t, rs, wave, L, smem, cp, sl, acc);
+        }
+        wait_vmcnt<0>();  // no copy may still be writing this workgroup's LDS
+    }
+
+    // K tile t of the V_DIRECT loop; its step s uses register slot (P + s) & 1.
+    template <int P>
+    static __device__ __forceinline__ void tile_direct(const GemmArgs& p, int m0, int n0, int t, int rs,
+                                                       int wave, const Lanes& L, SPT_LDS char* smem,
+                                                       const Copy& cp, Slot (&sl)[2], acc_t (&acc)[C::FM][C::FN])
+    {
+        const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+        const SPT_LDS char* cur = smem + rs * C::STAGE_BYTES;
+        const int rs_next = rs + 1 == C::S ? 0 : rs + 1;
+        const Dma none{};
+#pragma unroll
+        for (int s = 0; s < C::KS; ++s) {
+            Slot& use = sl[(P + s) & 1];
+            Slot& nxt = sl[(P + s + 1) & 1];
+            if (s + 1 < C::KS) {
+                step<0, true>(use, nxt, cur, s + 1, L, none, wave, cp, acc);
+                continue;
+            }
+            wait_lgkmcnt0();                       // this wave's reads of tile t are complete
+            wait_vmcnt<(C::S - 2) * C::LOADS>();   // its copies of tile t+1 have landed
+            barrier();                             // tile t+1 visible to all; tile t's stage free
+            const Dma d = dma_begin(p, m0, n0, t + C::S, lds0 + rs * C::STAGE_BYTES);
+            step<C::LOADS, true>(use, nxt, smem + rs_next * C::STAGE_BYTES, 0, L, d, wave, cp, acc);
+        }
+    }
+
     static __device__ __forceinline__ void run(const GemmArgs& p)
     {
         __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS_BYTES];
@@ -553,11 +749,12 @@ struct Gemm {
         tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
         const int m0 = tm * C::BM, n0 = tn * C::BN;
         const int wm0 = (wave / C::WAVES_N) * C::WTM, wn0 = (wave % C::WAVES_N) * C::WTN;
+        const int mb0 = wm0 / 16, nb0 = wn0 / 16;
 
         Copy cp;
         setup_copy(p, m0, n0, tid, cp);
-        Frag fr;
-        setup_frag(wm0, wn0, lane, fr);
+        Lanes L;
+        setup_lanes(lane, mb0, nb0, L);
 
         acc_t acc[C::FM][C::FN];
 #pragma unroll
@@ -576,7 +773,7 @@ struct Gemm {
                 store_regs(smem, tid, ra, rb);
                 wait_lgkmcnt0();
                 barrier();
-                compute(smem, fr, acc);
+                compute(smem, L, wave, cp, acc);
                 barrier();
             }
         } else if constexpr (C::V == V_REG) {
@@ -592,7 +789,7 @@ struct Gemm {
                 SPT_LDS char* nxt = smem + (C::S == 2 ? ((t + 1) & 1) : 0) * C::STAGE_BYTES;
                 const bool more = t + 1 < nf;
                 if (more) load_regs(p, m0, n0, t + 1, cp, ra, rb);  // in flight during compute
-                compute(cur, fr, acc);
+                compute(cur, L, wave, cp, acc);
                 if constexpr (C::S == 1) barrier();  // one buffer: all reads of it done first
                 if (more) {
                     wait_vmcnt<0>();
@@ -602,46 +799,31 @@ struct Gemm {
                 barrier();
             }
         } else {
-            // V_DIRECT: S-stage ring.  Prologue: tiles 0..S-2 into stages 0..S-2.
-#pragma unroll
-            for (int i = 0; i < C::S - 1; ++i)
-                if (i < nf) issue_direct(p, m0, n0, i, smem + i * C::STAGE_BYTES, wave, cp);
-            int rs = 0;           // read stage (consumer)
-            int ws = C::S - 1;    // write stage (producer)
-            for (int t = 0; t < nf; ++t) {
-                if (t + C::S - 2 < nf)
-                    wait_vmcnt<(C::S - 2) * C::LOADS>();  // tiles t+1..t+S-2 may stay in flight
-                else
-                    wait_vmcnt<0>();
-                barrier();
-                if (t + C::S - 1 < nf) {
-                    issue_direct(p, m0, n0, t + C::S - 1, smem + ws * C::STAGE_BYTES, wave, cp);
-                    ws = ws + 1 == C::S ? 0 : ws + 1;
-                }
-                compute(smem + rs * C::STAGE_BYTES, fr, acc);
-                rs = rs + 1 == C::S ? 0 : rs + 1;
-            }
+            loop_direct(p, m0, n0, wave, L, smem, cp, acc);
         }
 
-        if (p.k_tail) {  // partial last tile, zero-filled beyond K, through VGPRs
+        if (!C::EXACT && p.k_tail) {  // partial last tile, zero-filled beyond K, through VGPRs
             load_tail(p, m0, n0, tid, ra, rb);
             wait_vmcnt<0>();
+            wait_lgkmcnt0();
             barrier();  // every wave is done reading the stages
             store_regs(smem, tid, ra, rb);
             wait_lgkmcnt0();
             barrier();
-            compute(smem, fr, acc);
+            compute(smem, L, wave, cp, acc);
         }
 
         store_c(p, m0, n0, wm0, wn0, lane, acc);
     }
 };
 
-// Two waves per SIMD: two 256-thread workgroups, or one 512-thread workgroup,
-// per CU; the compiler keeps VGPR + AGPR use within 256 per lane.
+// Two waves per SIMD (two 256-thread workgroups, or one 512-thread workgroup,
+// per CU) keep VGPR + AGPR use within 256 per lane; a 128 x 128 wave tile
+// runs one wave per SIMD with up to 512.
 template <class C>
 __global__ __attribute__((amdgpu_flat_work_group_size(C::THREADS, C::THREADS),
-                          amdgpu_waves_per_eu(2, 2))) void gemm_kernel(GemmArgs p)
+                          amdgpu_waves_per_eu(C::WAVES_PER_SIMD, C::WAVES_PER_SIMD))) void
+gemm_kernel(GemmArgs p)
 {
     Gemm<C>::run(p);
 }

@@ -11,7 +11,7 @@ namespace spt {
 typedef hipError_t (*LaunchFn)(const GemmArgs&, unsigned grid, hipStream_t);
 
 struct KernelEntry {
-    int dtype, bcol, tile, variant, stages;
+    int dtype, bcol, tile, variant, stages, exact;
     int threads, lds_bytes, loads_per_tile;
     LaunchFn launch;
     const void* kernel;
@@ -27,7 +27,8 @@ KernelTable kernels_bf16();
 KernelTable kernels_i8();
 KernelTable kernels_f32();
 
-// nullptr when that combination is not built.
-const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int stages);
+// nullptr when that combination is not built.  exact = 1 asks for the
+// instantiation that assumes M, N, K are multiples of the tile.
+const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int stages, int exact);
 
 }  // namespace spt

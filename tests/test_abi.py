@@ -62,6 +62,7 @@ def ex(M=64, N=64, K=64, A=PA, lda=None, B=PB, ldb=None, C=PC, ldc=None, dtype=s
     (dict(var=spt.VARIANT_SYNC, st=2), -2), (dict(var=spt.VARIANT_DIRECT, st=1), -2),
     (dict(var=spt.VARIANT_REG, st=3), -2), (dict(dtype=spt.I8, K=131072), -2),
     (dict(var=spt.VARIANT_DIRECT, st=3, tile=spt.TILE_256x256), -2),
+    (dict(var=spt.VARIANT_DIRECT, st=3, tile=spt.TILE_256x256_4W), -2), (dict(tile=5), -1),
     (dict(A=PA + 8), -3), (dict(B=PB + 2), -3), (dict(C=PC + 4), -3),
     (dict(K=60, lda=60), -3), (dict(N=60, ldb=60, ldc=64), -3), (dict(N=62, ldc=62), -3),
 ])
@@ -87,20 +88,18 @@ def test_plan_rejects_what_gemm_rejects(L):
 DTYPES = [(spt.F16, 2), (spt.BF16, 2), (spt.I8, 1), (spt.F32, 4)]
 PAIRS = [(spt.VARIANT_SYNC, 1), (spt.VARIANT_REG, 1), (spt.VARIANT_REG, 2), (spt.VARIANT_DIRECT, 2),
          (spt.VARIANT_DIRECT, 3)]
-TILES = {1: (128, 256, 64, 256), 2: (256, 256, 128, 512), 3: (128, 128, 64, 256)}
+TILES = {1: (128, 256, 64, 256), 2: (256, 256, 128, 512), 3: (128, 128, 64, 256), 4: (256, 256, 128, 256)}
 
 
 @pytest.mark.parametrize("dtype,elt", DTYPES)
-@pytest.mark.parametrize("tile", [1, 2, 3])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4])
 @pytest.mark.parametrize("var,st", PAIRS)
 def test_plan_matches_page_formulas(L, dtype, elt, tile, var, st):
     BM, BN, BKB, thr = TILES[tile]
     BK = BKB // elt
     M, N, K = 4000, 3000, 1000
     rc, pi = spt.spt_plan(dtype, M, N, K, spt.ROW, var, st, tile)
-    if tile == 2 and st == 3:
-        assert rc == 0  # the plan exists; the kernel is not built (160 KiB LDS)
-    assert rc == 0
+    assert rc == 0  # (256 x 256 tiles with 3 stages: planned, not built -- 192 KiB of LDS)
     assert (pi.BM, pi.BN, pi.BK, pi.threads) == (BM, BN, BK, thr)
     assert pi.stage_bytes == P.stage_bytes(BM, BN, BK, elt)
     assert pi.a_stage_bytes == BM * BK * elt and pi.b_stage_bytes == BK * BN * elt
