@@ -73,11 +73,13 @@ enum spt_layout { SPT_ROW = 0, SPT_COL = 1 };
  *          1 LDS stage (register-only prefetch) or 2 (double buffer).
  *  DIRECT  asynchronous global->LDS copies (the pages' cp.async variant,
  *          on CDNA4 the buffer_load ... lds instruction, which bypasses the
- *          VGPRs), in an S-stage LDS ring with S = 2 or 3 ("Hiding Memory
+ *          VGPRs), in an S-stage LDS ring with S = 2, 3 or 4 ("Hiding Memory
  *          Latency ...", sections 5 and 6).
  *  AUTO    the library's choice for the shape.
- * Valid (variant, stages) pairs: SYNC x 1, REG x {1,2}, DIRECT x {2,3};
- * stages = 0 picks the variant's default (SYNC 1, REG 2, DIRECT 3).
+ * Valid (variant, stages) pairs: SYNC x 1, REG x {1,2}, DIRECT x {2,3,4};
+ * a ring of S stages must fit in the 160 KiB of LDS (SPT_ERR_UNSUPPORTED
+ * otherwise).  stages = 0 picks the variant's default (SYNC 1, REG 2,
+ * DIRECT 2 for tiles with a 128-byte K depth, else 3).
  */
 enum spt_variant {
     SPT_VARIANT_AUTO = 0,
@@ -87,29 +89,36 @@ enum spt_variant {
 };
 
 /*
- * Workgroup tile menu.  The K depth of a tile is 64 bytes of each row for
- * SPT_TILE_128x256 (BK = 32 for fp16/bf16, 64 for int8, 16 for fp32) and
- * 128 bytes for SPT_TILE_256x256.
- *  SPT_TILE_128x256  128 x 256, 256 threads (2 x 2 waves of 64 x 128): the
- *                    tile of "Hiding Memory Latency ...", section 6.
- *  SPT_TILE_256x256  256 x 256, 512 threads (2 x 4 waves of 128 x 64).
- *  SPT_TILE_128x128  128 x 128, 256 threads (2 x 2 waves of 64 x 64).
- *  SPT_TILE_256x256_4W  256 x 256, 256 threads (2 x 2 waves of 128 x 128,
- *                    one wave per SIMD).
+ * Workgroup tile menu.  The K depth of a tile is 64 bytes of each row (BK =
+ * 32 for fp16/bf16, 64 for int8, 16 for fp32) or 128 bytes (twice that).
+ *  SPT_TILE_128x256  128 x 256, 64-byte K depth, 256 threads (2 x 2 waves
+ *                    of 64 x 128): the tile of "Hiding Memory Latency ...",
+ *                    section 6.
+ *  SPT_TILE_256x256  256 x 256, 128-byte K depth, 512 threads (2 x 4 waves
+ *                    of 128 x 64).
+ *  SPT_TILE_128x128  128 x 128, 64-byte K depth, 256 threads (2 x 2 waves
+ *                    of 64 x 64).
+ *  SPT_TILE_256x256_4W  256 x 256, 128-byte K depth, 256 threads (2 x 2
+ *                    waves of 128 x 128, one wave per SIMD).
+ *  SPT_TILE_256x256_4W_K64B  the same with a 64-byte K depth (room for a
+ *                    3- or 4-stage ring).
  */
 enum spt_tile {
     SPT_TILE_AUTO = 0,
     SPT_TILE_128x256 = 1,
     SPT_TILE_256x256 = 2,
     SPT_TILE_128x128 = 3,
-    SPT_TILE_256x256_4W = 4
+    SPT_TILE_256x256_4W = 4,
+    SPT_TILE_256x256_4W_K64B = 5
 };
 
 enum spt_status {
     SPT_OK = 0,
     SPT_ERR_INVALID = -1,     /* negative size, null pointer, pitch too small, bad enum */
     SPT_ERR_UNSUPPORTED = -2, /* (variant, stages, tile, dtype, layout) not built; int8 K > 131071;
-                                 an operand panel too large for 32-bit buffer offsets */
+                                 an operand panel too large for 32-bit buffer offsets; A or B
+                                 below 64 KiB or at or above 2^47 (the 48-bit base of a buffer
+                                 descriptor) */
     SPT_ERR_MISALIGNED = -3,  /* pointer or row pitch not a multiple of 16 bytes */
     SPT_ERR_LAUNCH = -4       /* the HIP launch reported an error */
 };

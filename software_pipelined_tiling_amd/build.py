@@ -18,8 +18,8 @@ LIB = os.path.join(HERE, "libspt.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["spt_kernels_f16.hip", "spt_kernels_bf16.hip", "spt_kernels_i8.hip",
-           "spt_kernels_f32.hip", "spt_api.cpp"]
+SOURCES = [f"spt_kernels_{dt}_{lay}.hip" for dt in ("f16", "bf16", "i8", "f32") for lay in ("row", "col")]
+SOURCES.append("spt_api.cpp")
 HEADERS = ["spt_kernel.hpp", "spt_instances.hpp", "spt_registry.h", "spt_config.h"]
 
 # Packed-fp32 VALU instructions are disabled for all device code (-packed-fp32-ops).
@@ -37,15 +37,24 @@ def _compile(src: str, defines=(), tag: str = "") -> str:
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = True, defines=(), out: str | None = None) -> str:
+def build(jobs: int | None = None, verbose: bool = True, defines=(), out: str | None = None,
+          reuse: bool = False, only=()) -> str:
     """Compile every source for gfx950 and link libspt.so (or `out`); returns its path.
 
-    `defines` are extra preprocessor definitions (tuning experiments only)."""
+    `defines` are extra preprocessor definitions (tuning experiments only).
+    With `reuse`, sources not listed in `only` keep their existing object file."""
     os.makedirs(BUILD, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 4)
     tag = "" if not defines else "_" + str(abs(hash(tuple(defines))))
+
+    def obj(src):
+        o = os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
+        if reuse and src not in only and os.path.exists(o):
+            return o
+        return _compile(src, defines, tag)
+
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda src: _compile(src, defines, tag), SOURCES))
+        objs = list(ex.map(obj, SOURCES))
     lib = out or LIB
     tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
@@ -58,7 +67,7 @@ def build(jobs: int | None = None, verbose: bool = True, defines=(), out: str | 
     return lib
 
 
-def asm(src: str = "spt_kernels_f16.hip", out: str | None = None) -> str:
+def asm(src: str = "spt_kernels_f16_row.hip", out: str | None = None) -> str:
     """gfx950 assembly of one kernel translation unit (for the ISA checks)."""
     os.makedirs(BUILD, exist_ok=True)
     out = out or os.path.join(BUILD, os.path.splitext(src)[0] + ".s")

@@ -25,16 +25,19 @@ static int fail(int status, const char* fmt, ...)
     return status;
 }
 
-static const KernelTable& table_for(int dtype)
+static const KernelTable& table_for(int dtype, int bcol)
 {
-    static const KernelTable t[4] = {kernels_f16(), kernels_bf16(), kernels_i8(), kernels_f32()};
-    return t[dtype];
+    static const KernelTable t[4][2] = {{kernels_f16_row(), kernels_f16_col()},
+                                        {kernels_bf16_row(), kernels_bf16_col()},
+                                        {kernels_i8_row(), kernels_i8_col()},
+                                        {kernels_f32_row(), kernels_f32_col()}};
+    return t[dtype][bcol ? 1 : 0];
 }
 
 const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int stages, int exact)
 {
     if (dtype < 0 || dtype > 3) return nullptr;
-    const KernelTable& t = table_for(dtype);
+    const KernelTable& t = table_for(dtype, bcol);
     for (int i = 0; i < t.count; ++i) {
         const KernelEntry& e = t.entries[i];
         if (e.bcol == bcol && e.tile == tile && e.variant == variant && e.stages == stages && e.exact == exact)
@@ -43,11 +46,20 @@ const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int s
     return nullptr;
 }
 
-// The library's default when the caller passes AUTO: the 3-stage DIRECT ring
-// on the 128 x 256 tile.
-static void resolve(int& variant, int& stages, int& tile)
+// The library's default when the caller passes AUTO.  Tile: the largest
+// whose grid still gives each of the 256 CUs a workgroup (256 x 256 with one
+// wave per SIMD carries the least LDS and global traffic per MFMA), else the
+// 128 x 256 tile if it does, else 128 x 128 for the most workgroups.
+// Variant: the DIRECT ring, 2 stages for 128-byte K tiles (two fill the LDS),
+// else 3.
+static constexpr int64_t kCus = 256;
+static void resolve(int64_t M, int64_t N, int& variant, int& stages, int& tile)
 {
-    if (tile == 0) tile = 1;
+    if (tile == 0) {
+        const int64_t n4 = ((M + 255) / 256) * ((N + 255) / 256);
+        const int64_t n1 = ((M + 127) / 128) * ((N + 255) / 256);
+        tile = n4 >= kCus ? 4 : n1 >= kCus ? 1 : 3;
+    }
     if (variant == V_AUTO) variant = V_DIRECT;
     if (stages == 0) stages = variant == V_SYNC ? 1 : variant == V_REG ? 2 : (kTiles[tile].BKB >= 128 ? 2 : 3);
 }
@@ -55,7 +67,7 @@ static void resolve(int& variant, int& stages, int& tile)
 static bool valid_pair(int variant, int stages)
 {
     return (variant == V_SYNC && stages == 1) || (variant == V_REG && (stages == 1 || stages == 2)) ||
-           (variant == V_DIRECT && (stages == 2 || stages == 3));
+           (variant == V_DIRECT && stages >= 2 && stages <= 4);
 }
 
 // Checks every argument except the pointers; fills `pi` on success.
@@ -66,13 +78,13 @@ static int make_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, i
     if (b_layout != SPT_ROW && b_layout != SPT_COL)
         return fail(SPT_ERR_INVALID, "b_layout %d is not an spt_layout", b_layout);
     if (variant < 0 || variant > 3) return fail(SPT_ERR_INVALID, "variant %d is not an spt_variant", variant);
-    if (stages < 0 || stages > 3) return fail(SPT_ERR_INVALID, "stages %d not in 0..3", stages);
+    if (stages < 0 || stages > 4) return fail(SPT_ERR_INVALID, "stages %d not in 0..4", stages);
     if (tile < 0 || tile >= kNumTiles) return fail(SPT_ERR_INVALID, "tile_id %d is not an spt_tile", tile);
     if (M < 0 || N < 0 || K < 0) return fail(SPT_ERR_INVALID, "negative size");
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(SPT_ERR_UNSUPPORTED, "size above 2^31-1");
     if (dtype == DT_I8 && K > 131071)
         return fail(SPT_ERR_UNSUPPORTED, "int8 K=%lld exceeds 131071 (exact int32 sum)", (long long)K);
-    resolve(variant, stages, tile);
+    resolve(M, N, variant, stages, tile);
     if (!valid_pair(variant, stages))
         return fail(SPT_ERR_UNSUPPORTED, "variant %d has no %d-stage form", variant, stages);
 
@@ -104,6 +116,9 @@ static int make_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, i
     p.b_stage_bytes = p.BK * p.BN * elt;
     p.stage_bytes = p.a_stage_bytes + p.b_stage_bytes;
     p.lds_bytes = stages * p.stage_bytes;
+    if (p.lds_bytes > kLdsPerCu)
+        return fail(SPT_ERR_UNSUPPORTED, "a %d-stage ring of %d-byte stages exceeds the 160 KiB of LDS", stages,
+                    p.stage_bytes);
     // "Hiding Memory Latency ...", section 6: 16-byte accesses per thread per stage.
     p.a_copies_per_thread = p.a_stage_bytes / 16 / p.threads;
     p.b_copies_per_thread = p.b_stage_bytes / 16 / p.threads;
@@ -145,6 +160,10 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     if (((uintptr_t)C % 16) || (ldc * 4) % 16) return fail(SPT_ERR_MISALIGNED, "C or ldc not 16-byte aligned");
     if (K > 0 && (((uintptr_t)A % 16) || ((uintptr_t)B % 16) || (lda * elt) % 16 || (ldb * elt) % 16))
         return fail(SPT_ERR_MISALIGNED, "A, B, lda or ldb not 16-byte aligned");
+    // Buffer descriptors hold 48-bit base addresses (the copy path lowers a
+    // base by a few KiB before adding offsets back).
+    if (K > 0 && ((uintptr_t)A >> 47 || (uintptr_t)B >> 47 || (uintptr_t)A < 65536 || (uintptr_t)B < 65536))
+        return fail(SPT_ERR_UNSUPPORTED, "A or B outside the device address range of buffer descriptors");
     // Byte offsets inside one workgroup's operand panel are 32-bit buffer offsets.
     const int64_t lim = INT64_C(0x7ffffff0);
     if ((int64_t)pi.BM * lda * elt >= lim || (bcol ? (int64_t)pi.BN * ldb * elt : (int64_t)pi.BK * ldb * elt) >= lim)
@@ -153,7 +172,10 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
 
     // The exact-fit instantiation when M, N and K are multiples of the tile
     // (same arithmetic, no tail or edge code), else the general one.
-    const bool fits = M % pi.BM == 0 && N % pi.BN == 0 && pi.k_tail == 0;
+    // A tile of one 64-byte MFMA k-step runs its ring in pairs of tiles (the
+    // register slot of step 0 alternates); the exact-fit form has no odd last tile.
+    const bool one_step = kTiles[pi.tile_id].BKB == 64;
+    const bool fits = M % pi.BM == 0 && N % pi.BN == 0 && pi.k_tail == 0 && (!one_step || pi.k_full_tiles % 2 == 0);
     const KernelEntry* e = fits ? find_kernel(dtype, bcol, pi.tile_id, pi.variant, pi.stages, 1) : nullptr;
     if (!e) e = find_kernel(dtype, bcol, pi.tile_id, pi.variant, pi.stages, 0);
     if (!e) return fail(SPT_ERR_UNSUPPORTED, "no kernel built for dtype %d layout %d tile %d variant %d stages %d",

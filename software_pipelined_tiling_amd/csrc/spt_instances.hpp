@@ -27,22 +27,24 @@ constexpr KernelEntry entry()
 #define SPT_PAIRS(DT, BC, TI)                                                              \
     entry<DT, BC, TI, V_SYNC, 1>(), entry<DT, BC, TI, V_REG, 1>(), entry<DT, BC, TI, V_REG, 2>(), \
         entry<DT, BC, TI, V_DIRECT, 2>()
-// The 3-stage ring where it fits in LDS (the 256 x 256 tiles need 3 x 64 KiB).
+// The 3- and 4-stage rings where they fit in LDS (not the 256 x 256 x 64-byte
+// tiles: 3 x 64 KiB).
 #define SPT_RING3(DT, BC, TI) entry<DT, BC, TI, V_DIRECT, 3>()
+#define SPT_RING34(DT, BC, TI) entry<DT, BC, TI, V_DIRECT, 3>(), entry<DT, BC, TI, V_DIRECT, 4>()
 
 // Exact-fit instantiations of the ring variants (no K tail, no edge checks).
 #define SPT_EXACT(DT, BC, TI) entry<DT, BC, TI, V_DIRECT, 2, 1>()
-#define SPT_EXACT3(DT, BC, TI) entry<DT, BC, TI, V_DIRECT, 3, 1>()
+#define SPT_EXACT34(DT, BC, TI) entry<DT, BC, TI, V_DIRECT, 3, 1>(), entry<DT, BC, TI, V_DIRECT, 4, 1>()
 
-#define SPT_DEFINE_TABLE(NAME, DT)                                                          \
-    static const KernelEntry k_##NAME[] = {                                                \
-        SPT_PAIRS(DT, 0, 1), SPT_RING3(DT, 0, 1), SPT_PAIRS(DT, 1, 1), SPT_RING3(DT, 1, 1), \
-        SPT_PAIRS(DT, 0, 2), SPT_PAIRS(DT, 1, 2),                                          \
-        SPT_PAIRS(DT, 0, 3), SPT_RING3(DT, 0, 3), SPT_PAIRS(DT, 1, 3), SPT_RING3(DT, 1, 3), \
-        SPT_PAIRS(DT, 0, 4), SPT_PAIRS(DT, 1, 4),                                          \
-        SPT_EXACT(DT, 0, 1), SPT_EXACT3(DT, 0, 1), SPT_EXACT(DT, 1, 1), SPT_EXACT3(DT, 1, 1), \
-        SPT_EXACT(DT, 0, 2), SPT_EXACT(DT, 1, 2), SPT_EXACT(DT, 0, 4), SPT_EXACT(DT, 1, 4), \
-    };                                                                                     \
+#define SPT_TILE_ALL(DT, BC, TI) SPT_PAIRS(DT, BC, TI), SPT_RING34(DT, BC, TI), SPT_EXACT(DT, BC, TI), SPT_EXACT34(DT, BC, TI)
+#define SPT_TILE_BIG(DT, BC, TI) SPT_PAIRS(DT, BC, TI), SPT_EXACT(DT, BC, TI)
+
+// The table of one (element type, B layout): NAME is e.g. f16_row.
+#define SPT_DEFINE_TABLE(NAME, DT, BC)                                                          \
+    static const KernelEntry k_##NAME[] = {                                                    \
+        SPT_TILE_ALL(DT, BC, 1), SPT_TILE_BIG(DT, BC, 2), SPT_PAIRS(DT, BC, 3), SPT_RING34(DT, BC, 3), \
+        SPT_TILE_BIG(DT, BC, 4), SPT_TILE_ALL(DT, BC, 5),                                      \
+    };                                                                                         \
     KernelTable kernels_##NAME() { return KernelTable{k_##NAME, (int)(sizeof(k_##NAME) / sizeof(k_##NAME[0]))}; }
 
 }  // namespace spt

@@ -68,6 +68,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "spt_config.h"
 
 namespace spt {
@@ -93,14 +95,23 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 // Keep the instruction order written in the source around this point.
 __device__ __forceinline__ void order_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// f(integral_constant<int, I>) for I = B .. E-1, expanded at compile time (a
+// `#pragma unroll` loop may be left rolled when its body is large, and a
+// rolled loop would index the accumulator array at run time).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // EXACT_: M, N and K are multiples of the tile (no K tail, no edge checks in
 // the epilogue); the dispatcher selects it only for such shapes.
 // BLANE_: row-major B kept in the lane layout (fp32 B always is).
-#ifndef SPT_B_LANE_DEFAULT
-#define SPT_B_LANE_DEFAULT false
-#endif
-template <int DT_, bool BCOL_, int TILE_, int V_, int S_, bool EXACT_ = false, bool BLANE_ = SPT_B_LANE_DEFAULT>
+template <int DT_, bool BCOL_, int TILE_, int V_, int S_, bool EXACT_ = false, bool BLANE_ = false>
 struct Cfg {
     static constexpr int DT = DT_;
     static constexpr bool BCOL = BCOL_;
@@ -125,8 +136,10 @@ struct Cfg {
     static constexpr int A_CPT = A_BYTES / 16 / THREADS;  // 16-byte copies per thread per stage
     static constexpr int B_CPT = B_BYTES / 16 / THREADS;
     static constexpr int LOADS = A_CPT + B_CPT;            // vmcnt units per tile per thread
-    // 16x16 wave tiles of 128 x 128 need the whole register file: one wave per SIMD
-    static constexpr int WAVES_PER_SIMD = FM * FN > 32 ? 1 : 2;
+    // 16x16 wave tiles of 128 x 128 need the whole register file: one wave per
+    // SIMD; so does a ring that leaves LDS for one workgroup of four waves per CU
+    static constexpr int WG_PER_CU_LDS = kLdsPerCu / LDS_BYTES;
+    static constexpr int WAVES_PER_SIMD = (FM * FN > 32 || WG_PER_CU_LDS * WAVES < 8) ? 1 : 2;
 
     static_assert(BK % KSTEP == 0, "BK must hold whole MFMA steps");
     static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0,
@@ -135,7 +148,7 @@ struct Cfg {
     static_assert(LDS_BYTES <= kLdsPerCu, "LDS ring exceeds 160 KiB");
     static_assert(V_ != V_SYNC || S_ == 1, "SYNC has one stage");
     static_assert(V_ != V_REG || (S_ == 1 || S_ == 2), "REG has 1 or 2 stages");
-    static_assert(V_ != V_DIRECT || (S_ == 2 || S_ == 3), "DIRECT has 2 or 3 stages");
+    static_assert(V_ != V_DIRECT || (S_ >= 2 && S_ <= 4), "DIRECT has 2 to 4 stages");
     static_assert((S_ - 1) * LOADS < 64, "vmcnt range");
 };
 
@@ -178,29 +191,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, ui
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
 }
 
-// The same buffer descriptor as four SGPR words, for inline asm: base
-// address (48 bits, stride 0), num_records, and the gfx9 raw-buffer word 3.
-__device__ __forceinline__ i32x4_t rsrc_words(const char* base, uint32_t bytes)
-{
-    const uint64_t a = (uint64_t)(uintptr_t)base;
-    return (i32x4_t){(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
-}
-
 // One asynchronous 16-byte-per-lane copy global -> LDS (buffer_load_dwordx4
-// ... lds): lane l's 16 bytes at rsrc + voffset land at LDS byte lds + 16*l.
-// `lds` must be wave-uniform.  Written as inline asm so that the compiler
-// does not guard later LDS reads with waits of its own (it cannot tell the
-// ring stages apart and would drain every copy in flight); the ring's
-// s_waitcnt vmcnt + s_barrier placement is the only synchronisation.  M0
-// carries the LDS address; the s_nop covers the M0-write -> LDS-DMA hazard.
+// ... lds): lane l's 16 bytes at rsrc + voffset + OFF land at LDS byte
+// lds + OFF + 16*l (the immediate offset applies to both addresses, checked
+// on gfx950).  `lds` must be wave-uniform.  Written as inline asm so that the
+// compiler does not guard later LDS reads with waits of its own (it cannot
+// tell the ring stages apart and would drain every copy in flight); the
+// ring's s_waitcnt vmcnt + s_barrier placement is the only synchronisation.
+// M0 carries the LDS address.  NOP: the s_nop covering the M0-write ->
+// LDS-DMA hazard, needed by the first copy after M0 takes a new value; the
+// copies that follow in a group see the same M0 value.
+template <int OFF, bool NOP>
 __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t lds, int voffset)
 {
-    asm volatile(
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %0, %1, 0 offen lds"
-        :
-        : "v"(voffset), "s"(rsrc), "{m0}"(lds)
-        : "memory");
+    static_assert(OFF >= 0 && OFF < 4096, "12-bit immediate offset");
+    if constexpr (NOP)
+        asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen offset:%3 lds"
+                     :
+                     : "v"(voffset), "s"(rsrc), "{m0}"(lds), "n"(OFF)
+                     : "memory");
+    else
+        asm volatile("buffer_load_dwordx4 %0, %1, 0 offen offset:%3 lds"
+                     :
+                     : "v"(voffset), "s"(rsrc), "{m0}"(lds), "n"(OFF)
+                     : "memory");
 }
 
 // Zero the bytes of a 16-byte chunk from byte `valid` on (little-endian: the
@@ -284,11 +298,25 @@ struct Gemm {
         }
     }
 
+    // Stage chunk (16 bytes) moved by copy i (0 .. cpt-1) of thread tid: each
+    // wave's copies cover cpt consecutive 1 KiB blocks of the operand region,
+    // one block per copy, lane l at byte 16 l of it.
+    static __device__ __forceinline__ constexpr int chunk_of(int i, int tid, int cpt)
+    {
+        return ((tid >> 6) * cpt + i) * 64 + (tid & 63);
+    }
+
     // ---- fragment reads ---------------------------------------------------------
     // Per-lane LDS byte offsets of this wave's fragments within a stage, for
     // MFMA row 0 / column 0 of the wave tile; other rows / columns add an
     // immediate.  A fragment (m, s): 16 rows x the 16-byte chunk 4s + g.
-    static constexpr int B_OFFS = C::BCOL ? C::KS : (C::BLANE ? 1 : C::FN);
+    // Row layout: the swizzle only permutes column blocks within groups of BQ
+    // (4 for tr_b16, 8 for tr_b8; the wave's first block is a multiple of BQ),
+    // so blocks n and n + BQ sit 128 bytes apart in every k-row and one lane
+    // offset per n mod BQ serves all FN blocks.
+    static constexpr int BQ_ = C::ELT == 2 ? 4 : 8;
+    static constexpr int BQ = C::FN % BQ_ == 0 ? BQ_ : C::FN;
+    static constexpr int B_OFFS = C::BCOL ? C::KS : (C::BLANE ? 1 : BQ);
     struct Lanes {
         int a[C::KS];
         int b[B_OFFS];
@@ -308,7 +336,7 @@ struct Gemm {
             // tr_b16: lane (g, i) fetches k-row 8g + (i >> 2) (+ 4h + KSTEP s) at columns
             // 4 (i & 3) .. + 3 of column block nb; swz_n only sees k-row bits 0, 1.
 #pragma unroll
-            for (int n = 0; n < C::FN; ++n) {
+            for (int n = 0; n < BQ; ++n) {
                 const int kr = 8 * g + (l16 >> 2);
                 const int c = 2 * (nb0 + n) + ((l16 & 3) >> 1);
                 L.b[n] = C::A_BYTES + kr * RN + 16 * (c ^ swz_n(kr)) + 8 * (l16 & 1);
@@ -317,7 +345,7 @@ struct Gemm {
             // tr_b8: lane (g, i) fetches k-row 16g + (i >> 1) (+ 8h + KSTEP s) at columns
             // 8 (i & 1) .. + 7 of column block nb; swz_n only sees k-row bits 0..2.
 #pragma unroll
-            for (int n = 0; n < C::FN; ++n) {
+            for (int n = 0; n < BQ; ++n) {
                 const int kr = 16 * g + (l16 >> 1);
                 L.b[n] = C::A_BYTES + kr * RN + 16 * ((nb0 + n) ^ swz_n(kr)) + 8 * (l16 & 1);
             }
@@ -344,7 +372,7 @@ struct Gemm {
                 o0 = L.b[0] + (br_block(n, s, 0) - C::A_BYTES);
                 o1 = L.b[0] + (br_block(n, s, 1) - C::A_BYTES);
             } else {
-                o0 = L.b[n] + s * C::KSTEP * RN;
+                o0 = L.b[n % BQ] + (n / BQ) * 128 + s * C::KSTEP * RN;
                 o1 = o0 + (C::ELT == 2 ? 4 : 8) * RN;
             }
             if constexpr (C::ELT == 2) {
@@ -362,7 +390,16 @@ struct Gemm {
     }
 
     // Per-thread copy geometry (loop invariant): byte offsets of this thread's
-    // A and B chunks from the K tile's base.
+    // A and B chunks from the K tile's base.  V_DIRECT copies go in groups of
+    // four that share one M0 value: copy i adds the immediate (i mod 4) KiB to
+    // both its LDS and its global address, so its register offset is lowered
+    // by the same amount, and every offset is raised by DMA_BIAS (the
+    // descriptor base is lowered by as much) to keep it non-negative.
+    static constexpr int DMA_BIAS = 3072;
+    static __device__ __forceinline__ constexpr int dma_bias(int i)
+    {
+        return C::V == V_DIRECT ? DMA_BIAS - (i % 4) * 1024 : 0;
+    }
     struct Copy {
         int a_voff[C::A_CPT];
         int b_voff[C::B_CPT];
@@ -374,20 +411,20 @@ struct Gemm {
 #pragma unroll
         for (int i = 0; i < C::A_CPT; ++i) {
             int r, k;
-            a_src(i * C::THREADS + tid, r, k);
+            a_src(chunk_of(i, tid, C::A_CPT), r, k);
             r = min(r, rows_a - 1);  // M edge: any in-range row (its outputs are not stored)
-            cp.a_voff[i] = r * p.lda * C::ELT + k * C::ELT;
+            cp.a_voff[i] = r * p.lda * C::ELT + k * C::ELT + dma_bias(i);
         }
 #pragma unroll
         for (int i = 0; i < C::B_CPT; ++i) {
             int k, n;
-            b_src(i * C::THREADS + tid, k, n);
+            b_src(chunk_of(i, tid, C::B_CPT), k, n);
             if constexpr (C::BCOL) {
                 n = min(n, min(C::BN, p.N - n0) - 1);  // N edge
-                cp.b_voff[i] = n * p.ldb * C::ELT + k * C::ELT;
+                cp.b_voff[i] = n * p.ldb * C::ELT + k * C::ELT + dma_bias(i);
             } else {
                 if (n0 + n >= p.N) n = 0;  // N edge: any in-range chunk
-                cp.b_voff[i] = k * p.ldb * C::ELT + n * C::ELT;
+                cp.b_voff[i] = k * p.ldb * C::ELT + n * C::ELT + dma_bias(i);
             }
         }
     }
@@ -419,30 +456,92 @@ struct Gemm {
     }
 
     // ---- V_DIRECT producer ---------------------------------------------------
-    // Copy j (0 .. LOADS-1) of K tile t into the stage at LDS byte `st`: the
-    // copies of wave w, number i of an operand cover that operand's stage
-    // chunks [(i WAVES + w) 64, + 64).
+    // Wave-uniform producer state, advanced by a constant per K tile so that
+    // the steady loop spends a handful of scalar instructions per tile on it.
+    // Every full K tile reads the same extent from its base: the rows (A,
+    // column-major B) or k-rows (row-major B) it touches, which the caller
+    // guarantees readable and which fits the 31-bit buffer range (the host
+    // checks the panel).  Tiles past the last full one get extent 0: empty
+    // copies that move nothing and still count in vmcnt.
+    struct Ring {
+        i32x4_t qa, qb;    // descriptors of the next K tile to copy: base - DMA_BIAS, extent
+        uint64_t sa, sb;   // bytes between consecutive K tiles
+        uint32_t na, nb;   // extent (with DMA_BIAS) of a full K tile
+        int left;          // full K tiles not yet copied
+        uint32_t m0a, m0b; // LDS byte address of this wave's first A / B block in stage 0
+    };
+    static __device__ __forceinline__ i32x4_t desc(uint64_t base, uint32_t bytes)
+    {
+        // base < 2^47 (checked on the host): word 1 holds its high bits with stride 0
+        return (i32x4_t){(int)(uint32_t)base, (int)(uint32_t)(base >> 32), (int)bytes, 0x00020000};
+    }
+    static __device__ __forceinline__ void ring_init(const GemmArgs& p, int m0, int n0, int wave,
+                                                     const SPT_LDS char* smem, Ring& r)
+    {
+        const int rows_a = min(C::BM, p.M - m0);
+        const uint64_t a = (uint64_t)(uintptr_t)(p.A + (long long)m0 * p.lda * C::ELT) - DMA_BIAS;
+        r.sa = (uint64_t)C::BK * C::ELT;
+        r.na = (uint32_t)(((long long)(rows_a - 1) * p.lda + C::BK) * C::ELT) + DMA_BIAS;
+        uint64_t b;
+        if constexpr (C::BCOL) {
+            const int cols = min(C::BN, p.N - n0);
+            b = (uint64_t)(uintptr_t)(p.B + (long long)n0 * p.ldb * C::ELT) - DMA_BIAS;
+            r.sb = (uint64_t)C::BK * C::ELT;
+            r.nb = (uint32_t)(((long long)(cols - 1) * p.ldb + C::BK) * C::ELT) + DMA_BIAS;
+        } else {
+            b = (uint64_t)(uintptr_t)(p.B + (long long)n0 * C::ELT) - DMA_BIAS;
+            r.sb = (uint64_t)C::BK * p.ldb * C::ELT;
+            r.nb = (uint32_t)(((long long)C::BK * p.ldb - n0) * C::ELT) + DMA_BIAS;
+        }
+        r.left = p.k_full;
+        r.qa = desc(a, r.left > 0 ? r.na : 0u);
+        r.qb = desc(b, r.left > 0 ? r.nb : 0u);
+        const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+        r.m0a = lds0 + (uint32_t)(wave * C::A_CPT) * 1024u;
+        r.m0b = lds0 + (uint32_t)C::A_BYTES + (uint32_t)(wave * C::B_CPT) * 1024u;
+    }
+    // Ring bookkeeping after a tile's copies were taken, in three parts that
+    // the scheduler spreads over free MFMA slots: advance the A base, the B
+    // base (64-bit adds on the descriptor words), then the extents.
+    static __device__ __forceinline__ void add64(i32x4_t& q, uint64_t step)
+    {
+        uint64_t a = ((uint64_t)(uint32_t)q[1] << 32) | (uint32_t)q[0];
+        a += step;
+        q[0] = (int)(uint32_t)a;
+        q[1] = (int)(uint32_t)(a >> 32);
+    }
+    static __device__ __forceinline__ void ring_advance(Ring& r, int part)
+    {
+        if (part == 0) add64(r.qa, r.sa);
+        if (part == 1) add64(r.qb, r.sb);
+        if (part == 2) {
+            r.left -= 1;
+            r.qa[2] = (int)(r.left > 0 ? r.na : 0u);
+            r.qb[2] = (int)(r.left > 0 ? r.nb : 0u);
+        }
+    }
+
+    // The copies of one K tile into one stage: copy j < A_CPT of the wave moves
+    // A block j of its run of A_CPT blocks, copy A_CPT + i B block i.
     struct Dma {
         i32x4_t ra, rb;
-        uint32_t st;
+        uint32_t m0a, m0b;
     };
-    static __device__ __forceinline__ Dma dma_begin(const GemmArgs& p, int m0, int n0, int t, uint32_t st)
+    static __device__ __forceinline__ Dma dma_of(const Ring& r, uint32_t stage_off)
     {
-        const char *pa, *pb;
-        uint32_t na, nb;
-        const int tt = t < p.k_full ? t : 0;  // beyond the last full tile: an empty copy
-        span_a(p, m0, tt, pa, na);
-        span_b(p, n0, tt, pb, nb);
-        if (t >= p.k_full) na = nb = 0;
-        return Dma{rsrc_words(pa, na), rsrc_words(pb, nb), st};
+        return Dma{r.qa, r.qb, r.m0a + stage_off, r.m0b + stage_off};
     }
-    static __device__ __forceinline__ void dma_issue(const Dma& d, int j, int wave, const Copy& cp)
+    template <int J>
+    static __device__ __forceinline__ void dma_issue(const Dma& d, const Copy& cp)
     {
-        if (j < C::A_CPT)
-            dma16(d.ra, d.st + (j * C::WAVES + wave) * 1024, cp.a_voff[j]);
+        constexpr bool IS_A = J < C::A_CPT;
+        constexpr int i = IS_A ? J : J - C::A_CPT;  // copy index within the operand
+        constexpr int g = i / 4, e = i % 4;          // group of four sharing one M0 value
+        const uint32_t m0 = (IS_A ? d.m0a : d.m0b) + g * 4096;
+        if constexpr (IS_A)
+            dma16<e * 1024, e == 0>(d.ra, m0, cp.a_voff[i]);
         else
-            dma16(d.rb, d.st + C::A_BYTES + ((j - C::A_CPT) * C::WAVES + wave) * 1024,
-                  cp.b_voff[j - C::A_CPT]);
+            dma16<e * 1024, e == 0>(d.rb, m0, cp.b_voff[i]);
     }
 
     // ---- V_REG / V_SYNC producer: global -> VGPR -> LDS ------------------------
@@ -468,10 +567,10 @@ struct Gemm {
                                                       const i32x4_t (&rb_)[C::B_CPT])
     {
 #pragma unroll
-        for (int i = 0; i < C::A_CPT; ++i) *(SPT_LDS i32x4_t*)(st + (i * C::THREADS + tid) * 16) = ra_[i];
+        for (int i = 0; i < C::A_CPT; ++i) *(SPT_LDS i32x4_t*)(st + chunk_of(i, tid, C::A_CPT) * 16) = ra_[i];
 #pragma unroll
         for (int i = 0; i < C::B_CPT; ++i)
-            *(SPT_LDS i32x4_t*)(st + C::A_BYTES + (i * C::THREADS + tid) * 16) = rb_[i];
+            *(SPT_LDS i32x4_t*)(st + C::A_BYTES + chunk_of(i, tid, C::B_CPT) * 16) = rb_[i];
     }
 
     // The partial last K tile (t = k_full, K - t*BK = k_tail elements), through
@@ -490,7 +589,7 @@ struct Gemm {
 #pragma unroll
         for (int i = 0; i < C::A_CPT; ++i) {
             int r, k;
-            a_src(i * C::THREADS + tid, r, k);
+            a_src(chunk_of(i, tid, C::A_CPT), r, k);
             r = min(r, rows_a - 1);
             const int valid = kt - k;  // elements of this chunk below K
             const int voff = r * p.lda * C::ELT + (valid > 0 ? k * C::ELT : 0);
@@ -499,7 +598,7 @@ struct Gemm {
 #pragma unroll
         for (int i = 0; i < C::B_CPT; ++i) {
             int k, n;
-            b_src(i * C::THREADS + tid, k, n);
+            b_src(chunk_of(i, tid, C::B_CPT), k, n);
             if constexpr (C::BCOL) {
                 n = min(n, min(C::BN, p.N - n0) - 1);
                 const int valid = kt - k;
@@ -535,82 +634,109 @@ struct Gemm {
         mma<C::DT>(acc[m][n], slot[C::FM + n], slot[m]);
     }
 
-    // Slot in the MFMA sequence of one k-step after which the A fragment of row
-    // ma of the next step is read: once row ma has used the old one (so its
-    // registers are reused) and after the `lead` copies and FN B reads.
-    static constexpr int a_read_at(int ma, int lead)
+    // ---- issue plan of one k-step ------------------------------------------------
+    // With one wave per SIMD a wave issues at most one instruction every four
+    // cycles, so a 16-cycle MFMA leaves room for about three more before the
+    // next MFMA is delayed.  Side work is therefore placed slot by slot (slot j
+    // = right after MFMA j): the FN B fragments of the next step in slots
+    // 0 .. FN-1 (each MFMA row needs all of them), A fragment ma of the next
+    // step once row ma has consumed the current one (its registers are then
+    // free), and copies and ring bookkeeping spread over the remaining slots.
+    static constexpr int NJ = C::FM * C::FN;
+    static constexpr int a_read_at(int ma)
     {
-        return (ma * C::FN + C::FN - 1) > (lead + C::FN + ma) ? (ma * C::FN + C::FN - 1) : (lead + C::FN + ma);
+        return (ma * C::FN + C::FN - 1) > (C::FN + ma) ? (ma * C::FN + C::FN - 1) : (C::FN + ma);
+    }
+    static constexpr int a_owner(int j)  // A fragment read after slot j, or -1
+    {
+        for (int ma = 0; ma < C::FM; ++ma)
+            if (a_read_at(ma) == j) return ma;
+        return -1;
+    }
+    static constexpr bool free_slot(int j) { return j >= C::FN && a_owner(j) < 0; }
+    static constexpr int NFREE = [] {
+        int n = 0;
+        for (int j = 0; j < NJ; ++j) n += free_slot(j);
+        return n;
+    }();
+    static constexpr int nth_free(int k)
+    {
+        for (int j = 0; j < NJ; ++j)
+            if (free_slot(j) && k-- == 0) return j;
+        return NJ;  // none left: after the last MFMA
+    }
+    // Copy d of NDMA: evenly over the free slots.
+    static constexpr int dma_at(int d, int ndma)
+    {
+        return ndma <= NFREE ? nth_free((d * NFREE) / ndma) : (d < NJ ? d : NJ);
+    }
+    static constexpr int dma_owner(int j, int ndma)
+    {
+        for (int d = 0; d < ndma; ++d)
+            if (dma_at(d, ndma) == j) return d;
+        return -1;
+    }
+    // Ring bookkeeping part q (0 .. 2): the last free slots that hold no copy.
+    static constexpr int adv_at(int q, int ndma)
+    {
+        int k = 2 - q;
+        for (int j = NJ - 1; j >= 0; --j)
+            if (free_slot(j) && dma_owner(j, ndma) < 0 && k-- == 0) return j;
+        return NJ;
+    }
+    static constexpr int adv_owner(int j, int ndma)
+    {
+        for (int q = 0; q < 3; ++q)
+            if (adv_at(q, ndma) == j) return q;
+        return -1;
     }
 
     // The FM x FN MFMAs of one k-step from `use`, row by row, with side work
-    // beside them in this order: NDMA copies (j < NDMA), then the FN B fragments
-    // of step `snext` of stage `src` into `nxt`, then its A fragments as rows
-    // free up (READ).  Every side instruction sits after one MFMA; a fence keeps
-    // the written order.
-    template <int NDMA, bool READ>
-    static __device__ __forceinline__ void step(const Slot& use, Slot& nxt, const SPT_LDS char* src, int snext,
-                                                const Lanes& L, const Dma& d, int wave, const Copy& cp,
+    // per the issue plan: the fragments of step `snext` of the stage that
+    // `src` + L address into `nxt` (READ), NDMA copies of `d`,
+    // and the ring bookkeeping (ADV).  A fence after every slot keeps the
+    // written order.
+    template <int NDMA, bool READ, bool ADV>
+    static __device__ __forceinline__ void step(const Slot& use, Slot& nxt, const SPT_LDS char* src, const Lanes& L,
+                                                int snext, const Dma& d, const Copy& cp, Ring& r,
                                                 acc_t (&acc)[C::FM][C::FN])
     {
-        constexpr int NJ = C::FM * C::FN;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
+        static_assert(!ADV || NDMA > 0, "bookkeeping belongs to the step that copies");
+        static_for<0, NJ>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            constexpr int dj = dma_owner(j, NDMA), aj = a_owner(j), qj = adv_owner(j, NDMA);
             mma_one(use, j, acc);
-            if (j < NDMA) dma_issue(d, j, wave, cp);
-            if (READ) {
-                const int nb = j - NDMA;
-                if (nb >= 0 && nb < C::FN) read_frag(src, L, snext, C::FM + nb, nxt);
-#pragma unroll
-                for (int ma = 0; ma < C::FM; ++ma)
-                    if (a_read_at(ma, NDMA) == j) read_frag(src, L, snext, ma, nxt);
-            }
+            if constexpr (dj >= 0) dma_issue<dj>(d, cp);
+            if constexpr (READ && j < C::FN) read_frag(src, L, snext, C::FM + j, nxt);
+            if constexpr (READ && aj >= 0) read_frag(src, L, snext, aj, nxt);
+            if constexpr (ADV && qj >= 0) ring_advance(r, qj);
             order_fence();
-        }
-        // side work whose slot fell beyond the last MFMA
-#pragma unroll
-        for (int j = NJ; j < NDMA; ++j) dma_issue(d, j, wave, cp);
-        if (READ) {
-#pragma unroll
-            for (int nb = 0; nb < C::FN; ++nb)
-                if (nb + NDMA >= NJ) read_frag(src, L, snext, C::FM + nb, nxt);
-#pragma unroll
-            for (int ma = 0; ma < C::FM; ++ma)
-                if (a_read_at(ma, NDMA) >= NJ) read_frag(src, L, snext, ma, nxt);
+        });
+        static_for<0, NDMA>([&](auto dc) {
+            constexpr int dd = decltype(dc)::value;
+            if constexpr (dma_at(dd, NDMA) >= NJ) dma_issue<dd>(d, cp);
+        });
+        if constexpr (ADV) {
+            static_for<0, 3>([&](auto qc) {
+                constexpr int q = decltype(qc)::value;
+                if constexpr (adv_at(q, NDMA) >= NJ) ring_advance(r, q);
+            });
         }
     }
 
     // One stage, all k-steps (REG / SYNC / the K tail): the fragments of step
     // s+1 are read beside the MFMAs of step s.
-    static __device__ __forceinline__ void compute(const SPT_LDS char* st, const Lanes& L, int wave,
-                                                   const Copy& cp, acc_t (&acc)[C::FM][C::FN])
+    static __device__ __forceinline__ void compute(const SPT_LDS char* st, const Lanes& L, const Copy& cp,
+                                                   acc_t (&acc)[C::FM][C::FN])
     {
         Slot sl[2];
         read_slot(st, L, 0, sl[0]);
         const Dma none{};
-#pragma unroll
-        for (int s = 0; s < C::KS; ++s) {
-            if (s + 1 < C::KS)
-                step<0, true>(sl[s & 1], sl[(s + 1) & 1], st, s + 1, L, none, wave, cp, acc);
-            else
-                step<0, false>(sl[s & 1], sl[(s + 1) & 1], st, 0, L, none, wave, cp, acc);
-        }
-    }
-
-    // Wait until at most n (0 .. S-1) younger tiles' copies are in flight.
-    static __device__ __forceinline__ void wait_tiles(int n)
-    {
-        if constexpr (C::S >= 3) {
-            if (n >= 2) {
-                wait_vmcnt<2 * C::LOADS>();
-                return;
-            }
-        }
-        if (n >= 1) {
-            wait_vmcnt<C::LOADS>();
-            return;
-        }
-        wait_vmcnt<0>();
+        Ring unused{};
+        static_for<0, C::KS>([&](auto sc) {
+            constexpr int s = decltype(sc)::value;
+            step<0, (s + 1 < C::KS), false>(sl[s & 1], sl[(s + 1) & 1], st, L, s + 1, none, cp, unused, acc);
+        });
     }
 
     // XCD-aware placement.  Workgroups are dispatched round-robin over the 8
@@ -669,72 +795,75 @@ struct Gemm {
     // iteration is the same: past the last K tile the ring issues empty copies
     // (a zero-length buffer range moves no memory, lanes read as out of range),
     // as "Hiding Memory Latency ...", section 8, turns out-of-range tiles into
-    // zero-filled stages, so the vmcnt count per tile never changes and the
-    // loop body has no branches.  The last tile's reads of "tile nf" are
-    // discarded; the ring is drained before the kernel leaves it.
+    // zero-filled stages, so the vmcnt count per tile never changes.  The
+    // stage index is a run-time value (a loop body per stage would hold more
+    // than the 256 accumulator registers of a 128 x 128 wave tile leave room
+    // for); an odd number of k-steps flips the register slot of step 0 every
+    // tile, so such tiles go in pairs to keep the slot a compile-time
+    // constant.  The last tile's reads of "tile nf" are discarded; the ring is
+    // drained before the kernel leaves.
     static __device__ __forceinline__ void loop_direct(const GemmArgs& p, int m0, int n0, int wave,
                                                        const Lanes& L, SPT_LDS char* smem, const Copy& cp,
                                                        acc_t (&acc)[C::FM][C::FN])
     {
         const int nf = p.k_full;
         if (nf == 0) return;
-        const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+        Ring r;
+        ring_init(p, m0, n0, wave, smem, r);
         // prologue: tiles 0 .. S-1 into stages 0 .. S-1
 #pragma unroll
         for (int i = 0; i < C::S; ++i) {
-            const Dma d = dma_begin(p, m0, n0, i, lds0 + i * C::STAGE_BYTES);
-#pragma unroll
-            for (int j = 0; j < C::LOADS; ++j) dma_issue(d, j, wave, cp);
+            const Dma d = dma_of(r, i * C::STAGE_BYTES);
+            static_for<0, C::LOADS>([&](auto jc) { dma_issue<decltype(jc)::value>(d, cp); });
+            ring_advance(r, 0);
+            ring_advance(r, 1);
+            ring_advance(r, 2);
         }
         wait_vmcnt<(C::S - 1) * C::LOADS>();  // tile 0 landed
         barrier();
         Slot sl[2];
         read_slot(smem, L, 0, sl[0]);
 
-        int t = 0, rs = 0;  // tile, and the stage it sits in
+        int t = 0;
+        uint32_t rs = 0;  // byte offset of the stage tile t sits in
         if constexpr (C::KS % 2 == 0) {
-            for (; t < nf; ++t) {
-                tile_direct<0>(p, m0, n0, t, rs, wave, L, smem, cp, sl, acc);
-                rs = rs + 1 == C::S ? 0 : rs + 1;
-            }
+            for (; t < nf; ++t) tile_direct<0>(r, rs, L, smem, cp, sl, acc);
         } else {
-            // an odd number of k-steps flips the register slot of step 0 every tile:
-            // tiles go in pairs so the slot stays a compile-time constant
             for (; t + 1 < nf; t += 2) {
-                tile_direct<0>(p, m0, n0, t, rs, wave, L, smem, cp, sl, acc);
-                rs = rs + 1 == C::S ? 0 : rs + 1;
-                tile_direct<1>(p, m0, n0, t + 1, rs, wave, L, smem, cp, sl, acc);
-                rs = rs + 1 == C::S ? 0 : rs + 1;
+                tile_direct<0>(r, rs, L, smem, cp, sl, acc);
+                tile_direct<1>(r, rs, L, smem, cp, sl, acc);
             }
-            if (t < nf) tile_direct<0>(p, m0, n0, t, rs, wave, L, smem, cp, sl, acc);
+            // (exact-fit kernels with one k-step per tile are dispatched for an even nf only)
+            if constexpr (!C::EXACT)
+                if (t < nf) tile_direct<0>(r, rs, L, smem, cp, sl, acc);
         }
         wait_vmcnt<0>();  // no copy may still be writing this workgroup's LDS
     }
 
-    // K tile t of the V_DIRECT loop; its step s uses register slot (P + s) & 1.
+    // One K tile in the stage at byte offset rs (advanced to the next stage on
+    // return); its k-step s uses register slot (P + s) & 1.
     template <int P>
-    static __device__ __forceinline__ void tile_direct(const GemmArgs& p, int m0, int n0, int t, int rs,
-                                                       int wave, const Lanes& L, SPT_LDS char* smem,
-                                                       const Copy& cp, Slot (&sl)[2], acc_t (&acc)[C::FM][C::FN])
+    static __device__ __forceinline__ void tile_direct(Ring& r, uint32_t& rs, const Lanes& L,
+                                                       const SPT_LDS char* smem, const Copy& cp, Slot (&sl)[2],
+                                                       acc_t (&acc)[C::FM][C::FN])
     {
-        const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-        const SPT_LDS char* cur = smem + rs * C::STAGE_BYTES;
-        const int rs_next = rs + 1 == C::S ? 0 : rs + 1;
+        const uint32_t nx = rs + C::STAGE_BYTES == (uint32_t)C::LDS_BYTES ? 0u : rs + C::STAGE_BYTES;
         const Dma none{};
-#pragma unroll
-        for (int s = 0; s < C::KS; ++s) {
+        static_for<0, C::KS>([&](auto sc) {
+            constexpr int s = decltype(sc)::value;
             Slot& use = sl[(P + s) & 1];
             Slot& nxt = sl[(P + s + 1) & 1];
-            if (s + 1 < C::KS) {
-                step<0, true>(use, nxt, cur, s + 1, L, none, wave, cp, acc);
-                continue;
+            if constexpr (s + 1 < C::KS) {
+                step<0, true, false>(use, nxt, smem + rs, L, s + 1, none, cp, r, acc);
+            } else {
+                wait_lgkmcnt0();                       // this wave's reads of this tile are complete
+                wait_vmcnt<(C::S - 2) * C::LOADS>();   // its copies of the next tile have landed
+                barrier();                             // next tile visible to all; this stage free
+                const Dma d = dma_of(r, rs);           // tile + S into this stage
+                step<C::LOADS, true, true>(use, nxt, smem + nx, L, 0, d, cp, r, acc);
             }
-            wait_lgkmcnt0();                       // this wave's reads of tile t are complete
-            wait_vmcnt<(C::S - 2) * C::LOADS>();   // its copies of tile t+1 have landed
-            barrier();                             // tile t+1 visible to all; tile t's stage free
-            const Dma d = dma_begin(p, m0, n0, t + C::S, lds0 + rs * C::STAGE_BYTES);
-            step<C::LOADS, true>(use, nxt, smem + rs_next * C::STAGE_BYTES, 0, L, d, wave, cp, acc);
-        }
+        });
+        rs = nx;
     }
 
     static __device__ __forceinline__ void run(const GemmArgs& p)
@@ -773,7 +902,7 @@ struct Gemm {
                 store_regs(smem, tid, ra, rb);
                 wait_lgkmcnt0();
                 barrier();
-                compute(smem, L, wave, cp, acc);
+                compute(smem, L, cp, acc);
                 barrier();
             }
         } else if constexpr (C::V == V_REG) {
@@ -789,7 +918,7 @@ struct Gemm {
                 SPT_LDS char* nxt = smem + (C::S == 2 ? ((t + 1) & 1) : 0) * C::STAGE_BYTES;
                 const bool more = t + 1 < nf;
                 if (more) load_regs(p, m0, n0, t + 1, cp, ra, rb);  // in flight during compute
-                compute(cur, L, wave, cp, acc);
+                compute(cur, L, cp, acc);
                 if constexpr (C::S == 1) barrier();  // one buffer: all reads of it done first
                 if (more) {
                     wait_vmcnt<0>();
@@ -810,7 +939,7 @@ struct Gemm {
             store_regs(smem, tid, ra, rb);
             wait_lgkmcnt0();
             barrier();
-            compute(smem, L, wave, cp, acc);
+            compute(smem, L, cp, acc);
         }
 
         store_c(p, m0, n0, wm0, wn0, lane, acc);

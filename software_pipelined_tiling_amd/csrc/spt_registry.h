@@ -22,10 +22,15 @@ struct KernelTable {
     int count;
 };
 
-KernelTable kernels_f16();
-KernelTable kernels_bf16();
-KernelTable kernels_i8();
-KernelTable kernels_f32();
+// One table per (element type, B layout), each in its own translation unit.
+KernelTable kernels_f16_row();
+KernelTable kernels_f16_col();
+KernelTable kernels_bf16_row();
+KernelTable kernels_bf16_col();
+KernelTable kernels_i8_row();
+KernelTable kernels_i8_col();
+KernelTable kernels_f32_row();
+KernelTable kernels_f32_col();
 
 // nullptr when that combination is not built.  exact = 1 asks for the
 // instantiation that assumes M, N, K are multiples of the tile.

@@ -20,14 +20,15 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-PAIRS = [("sync", 1), ("reg", 1), ("reg", 2), ("direct", 2), ("direct", 3)]
-TILES = [1, 2, 3, 4]
+PAIRS = [("sync", 1), ("reg", 1), ("reg", 2), ("direct", 2), ("direct", 3), ("direct", 4)]
+TILES = [1, 2, 3, 4, 5]
 SENT_F = np.uint32(0x7FC00ABC)   # a NaN payload no kernel produces
 SENT_I = np.int32(0x7FFFFFFF)
 
 
 def built(tile, variant, stages):
-    return not (tile in (2, 4) and variant == "direct" and stages == 3)
+    """Rings of 64 KiB stages (tiles 2 and 4) hold two stages at most in 160 KiB of LDS."""
+    return not (tile in (2, 4) and variant == "direct" and stages >= 3)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -248,9 +249,34 @@ def test_full_fp16_4096(oracle_mod, variant, stages):
     sampled(oracle_mod, I.W_F16_4096, variant, stages, 1)
 
 
-@pytest.mark.parametrize("variant,stages", [("auto", 0), ("sync", 1), ("direct", 2)])
-def test_full_int8_4096_bcol(oracle_mod, variant, stages):
-    sampled(oracle_mod, I.W_I8_4096, variant, stages, 1)
+@pytest.mark.parametrize("tile,stages", [(2, 2), (4, 2), (5, 2), (5, 3), (5, 4), (1, 4)])
+def test_full_fp16_4096_ring_tiles(oracle_mod, tile, stages):
+    """The exact-fit ring kernels of the other tiles at the full 4096^3 size."""
+    sampled(oracle_mod, I.W_F16_4096, "direct", stages, tile)
+
+
+@pytest.mark.parametrize("variant,stages,tile", [("auto", 0, 0), ("sync", 1, 1), ("direct", 2, 1),
+                                                 ("direct", 2, 4), ("direct", 3, 5)])
+def test_full_int8_4096_bcol(oracle_mod, variant, stages, tile):
+    sampled(oracle_mod, I.W_I8_4096, variant, stages, tile)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "i8"])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 96), (512, 256, 128), (256, 512, 192)])
+def test_exact_shapes_odd_and_even_k_tiles(oracle_mod, dtype, M, N, K):
+    """Tile-multiple shapes whose count of 64-byte K tiles is odd (general
+    kernel) or even (exact-fit kernel): every ring depth of the tiles with a
+    64-byte K depth agrees with the oracle and bit for bit with SYNC."""
+    A, B = operands(dtype, False, M, N, K, 11)
+    Cref = ref(oracle_mod, A, B, dtype, False, N, K)
+    for tile in (1, 3, 5):
+        outs = []
+        for v, s in [("sync", 1), ("direct", 2), ("direct", 3), ("direct", 4)]:
+            C = run(A, B, dtype, False, M, N, K, v, s, tile)
+            parity.check_full(C, Cref, A, B, dtype, False, M, N, K)
+            outs.append(C)
+        for C in outs[1:]:
+            assert np.array_equal(C.view(np.uint32), outs[0].view(np.uint32)), (tile, M, N, K)
 
 
 @pytest.mark.parametrize("K", I.LOWK_KS)
