@@ -15,7 +15,10 @@ Besides the headline value it reports, in the same line:
   sweep         every (tile, variant, stages) of the library on the
                 headline workload, the unpipelined one included
   workloads     int8 4096^3 (B column-major), bf16 8192^2 x K low-K sweep
-                (with HBM GB/s), bf16 4000x3000x1000 ragged
+                (with HBM GB/s), bf16 4000x3000x1000 ragged, fp16 256^3
+  power         socket power and GFX clocks sampled with amd-smi while the
+                headline kernel runs back to back for a few seconds, and the
+                dense peak at that clock (context for the roofline fraction)
 """
 from __future__ import annotations
 
@@ -33,7 +36,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "i8": 5033.2, "f32": 157.3}  # dense MFMA, MI355X
 HBM_GBS = 8000.0
-PAIRS = [("sync", 1), ("reg", 1), ("reg", 2), ("direct", 2), ("direct", 3)]
+PAIRS = [("sync", 1), ("reg", 1), ("reg", 2), ("direct", 2), ("direct", 3), ("direct", 4)]
+TILES = (1, 2, 3, 4, 5)
+FLOP_PER_CLK = {"f16": 256 * 4096, "bf16": 256 * 4096, "i8": 256 * 8192}  # dense MFMA, whole chip
 
 
 def kernel_source_hash() -> str:
@@ -117,7 +122,7 @@ def cpu_baseline(w, budget_s: float):
 def traffic_from_profile(kernel_sha: str):
     """HBM bytes per launch from committed rocprofv3 counter summaries, if they were
     taken on this exact kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", "hbm_traffic_fp16_4096.json")
+    p = os.path.join(ROOT, "profiles", "gemm_fp16_4096_hbm_traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -125,6 +130,61 @@ def traffic_from_profile(kernel_sha: str):
     if d.get("kernel_source_sha") != kernel_sha:
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+def sample_power(prob: "Problem", seconds: float):
+    """Run the headline call back to back for `seconds` while amd-smi samples
+    socket power and the GFX (XCD) clocks; None when amd-smi is unavailable."""
+    import re
+    import shutil
+    import subprocess
+    import threading
+    import torch
+    import software_pipelined_tiling_amd as spt
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    samples, stop = [], [False]
+
+    def poll():
+        while not stop[0]:
+            try:
+                txt = subprocess.run([exe, "metric", "-p", "-c"], capture_output=True, text=True,
+                                     timeout=20).stdout
+            except Exception:
+                return
+            pw = re.findall(r"SOCKET_POWER:\s*(\d+)", txt)
+            cl = [int(c) for c in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)", txt)]
+            if pw and cl:
+                samples.append((int(pw[0]), sum(cl) / len(cl)))
+            time.sleep(0.1)
+
+    a = prob.args(torch.cuda.current_stream().cuda_stream)
+    for _ in range(300):
+        spt.spt_gemm_ex(*a)
+    torch.cuda.synchronize()
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(100):
+            spt.spt_gemm_ex(*a)
+        torch.cuda.synchronize()
+        n += 100
+    dt = time.perf_counter() - t0
+    stop[0] = True
+    th.join(timeout=30)
+    if len(samples) < 3:
+        return None
+    busy = samples[len(samples) // 3:]  # past the ramp
+    watts = sorted(s[0] for s in busy)[len(busy) // 2]
+    mhz = sorted(s[1] for s in busy)[len(busy) // 2]
+    w = prob.w
+    return {"socket_power_w": watts, "gfx_clock_mhz": round(mhz), "samples": len(busy),
+            "sustained_tflops": round(w.flops * n / dt / 1e12, 1), "seconds": round(dt, 2),
+            "peak_tflops_at_clock": round(FLOP_PER_CLK[w.dtype] * mhz * 1e6 / 1e12, 1),
+            "source": "amd-smi metric -p -c, median after the first third of the samples"}
 
 
 def main():
@@ -139,7 +199,11 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=25.0, help="seconds of oracle CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-power", action="store_true", help="skip the amd-smi power / clock sample")
+    ap.add_argument("--power-seconds", type=float, default=3.0)
     ap.add_argument("--only-headline", action="store_true", help="headline workload only (profiling)")
+    ap.add_argument("--only-workload", default=None,
+                    help="time only this side workload by name prefix, e.g. 'bf16 GEMM 8192' (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain 256 MiB device copies (HBM counter scale)")
     args = ap.parse_args()
@@ -203,29 +267,38 @@ def main():
         out["copy_calibration_bytes"] = src.numel() * 4
         del src, dst
 
+    if not args.only_headline and not args.no_power:
+        out["power"] = sample_power(head, args.power_seconds)
+
+    if args.only_workload:
+        args.no_sweep = True
     if not args.only_headline:
         steps = max(20, min(args.steps, 100))
         if not args.no_sweep:
             sweep = []
-            for tile in (1, 2, 3):
+            for tile in TILES:
                 for v, s in PAIRS:
-                    t = time_calls(head, steps, 3, v, s, tile)
+                    t = time_calls(head, steps, 20, v, s, tile)
                     if t is None:
                         continue
                     sweep.append({"tile": tile, "variant": v, "stages": s, "us": round(t * 1e3, 2),
                                   "tflops": round(w.flops / (t * 1e-3) / 1e12, 1)})
             out["sweep"] = sweep
             by = {(d["tile"], d["variant"], d["stages"]): d["tflops"] for d in sweep}
-            base = by.get((1, "sync", 1))
-            if base:
-                out["pipelining_speedup_pages_tile"] = {
-                    f"{v}{s}": round(by[(1, v, s)] / base, 3) for v, s in PAIRS if (1, v, s) in by}
+            # speedup of each pipelined form over the unpipelined SYNC loop of the same tile:
+            # the pages' 128 x 256 x 32 tile, and the tile of the headline
+            for name, t in (("pipelining_speedup_pages_tile", 1), ("pipelining_speedup_headline_tile", plan.tile_id)):
+                base = by.get((t, "sync", 1))
+                if base:
+                    out[name] = {f"{v}{s}": round(by[(t, v, s)] / base, 3) for v, s in PAIRS if (t, v, s) in by}
         del head
         extra = {}
         for wk in [I.W_I8_4096, I.W_BF16_RAGGED, I.W_F16_256] + [I.w_bf16_lowk(k) for k in I.LOWK_KS]:
+            if args.only_workload and not wk.name.startswith(args.only_workload):
+                continue
             p = Problem(wk)
-            t = time_calls(p, steps, 3)
-            t1 = time_calls(p, steps, 3, "sync", 1)
+            t = time_calls(p, steps, 100)
+            t1 = time_calls(p, steps, 100, "sync", 1)
             peak = PEAK_TFLOPS[wk.dtype]
             tf = wk.flops / (t * 1e-3) / 1e12
             extra[wk.name] = {"us": round(t * 1e3, 2), "tflops": round(tf, 1),

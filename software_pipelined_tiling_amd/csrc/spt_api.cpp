@@ -46,19 +46,24 @@ const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int s
     return nullptr;
 }
 
-// The library's default when the caller passes AUTO.  Tile: the largest
-// whose grid still gives each of the 256 CUs a workgroup (256 x 256 with one
-// wave per SIMD carries the least LDS and global traffic per MFMA), else the
-// 128 x 256 tile if it does, else 128 x 128 for the most workgroups.
-// Variant: the DIRECT ring, 2 stages for 128-byte K tiles (two fill the LDS),
-// else 3.
+// The library's default when the caller passes AUTO (chosen from measured
+// sweeps on MI355X).  Tile: 256 x 256 with one wave per SIMD (the least LDS and
+// global traffic per MFMA) when the shape is an exact multiple of it, its grid
+// gives each of the 256 CUs a workgroup and K spans at least 512 bytes (short K
+// is bound by the C store, where two 128 x 256 workgroups per CU overlap
+// better); else the 128 x 256 tile if its grid fills the CUs; else 128 x 128
+// for the most workgroups.  Variant: the DIRECT ring, 2 stages for 128-byte K
+// tiles (two fill the LDS), else 3.
 static constexpr int64_t kCus = 256;
-static void resolve(int64_t M, int64_t N, int& variant, int& stages, int& tile)
+static void resolve(int dtype, int64_t M, int64_t N, int64_t K, int& variant, int& stages, int& tile)
 {
     if (tile == 0) {
-        const int64_t n4 = ((M + 255) / 256) * ((N + 255) / 256);
+        const int elt = elt_bytes(dtype);
+        const int64_t bk4 = kTiles[4].BKB / elt;
+        const bool fits4 = M % 256 == 0 && N % 256 == 0 && K % bk4 == 0 && K * elt >= 512;
+        const int64_t n4 = (M / 256) * (N / 256);
         const int64_t n1 = ((M + 127) / 128) * ((N + 255) / 256);
-        tile = n4 >= kCus ? 4 : n1 >= kCus ? 1 : 3;
+        tile = (fits4 && n4 >= kCus) ? 4 : n1 >= kCus ? 1 : 3;
     }
     if (variant == V_AUTO) variant = V_DIRECT;
     if (stages == 0) stages = variant == V_SYNC ? 1 : variant == V_REG ? 2 : (kTiles[tile].BKB >= 128 ? 2 : 3);
@@ -84,7 +89,7 @@ static int make_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, i
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(SPT_ERR_UNSUPPORTED, "size above 2^31-1");
     if (dtype == DT_I8 && K > 131071)
         return fail(SPT_ERR_UNSUPPORTED, "int8 K=%lld exceeds 131071 (exact int32 sum)", (long long)K);
-    resolve(M, N, variant, stages, tile);
+    resolve(dtype, M, N, K, variant, stages, tile);
     if (!valid_pair(variant, stages))
         return fail(SPT_ERR_UNSUPPORTED, "variant %d has no %d-stage form", variant, stages);
 

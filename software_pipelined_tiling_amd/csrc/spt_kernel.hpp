@@ -545,14 +545,18 @@ struct Gemm {
     }
 
     // ---- V_REG / V_SYNC producer: global -> VGPR -> LDS ------------------------
+    // Tile t (empty loads, which read as zero, for t >= k_full: the loop
+    // prefetches one tile past its end without a branch).
     static __device__ __forceinline__ void load_regs(const GemmArgs& p, int m0, int n0, int t,
                                                      const Copy& cp, i32x4_t (&ra_)[C::A_CPT],
                                                      i32x4_t (&rb_)[C::B_CPT])
     {
         const char *pa, *pb;
         uint32_t na, nb;
-        span_a(p, m0, t, pa, na);
-        span_b(p, n0, t, pb, nb);
+        const bool live = t < p.k_full;
+        span_a(p, m0, live ? t : 0, pa, na);
+        span_b(p, n0, live ? t : 0, pb, nb);
+        if (!live) na = nb = 0;
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(pa, na), rb = make_rsrc(pb, nb);
 #pragma unroll
         for (int i = 0; i < C::A_CPT; ++i) ra_[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, cp.a_voff[i], 0, 0);
@@ -913,17 +917,16 @@ struct Gemm {
                 wait_lgkmcnt0();
                 barrier();
             }
+            // tile t+1 is fetched while tile t is computed (past the end: an empty
+            // fetch whose zeros land in a stage nobody reads again)
             for (int t = 0; t < nf; ++t) {
                 SPT_LDS char* cur = smem + (C::S == 2 ? (t & 1) : 0) * C::STAGE_BYTES;
                 SPT_LDS char* nxt = smem + (C::S == 2 ? ((t + 1) & 1) : 0) * C::STAGE_BYTES;
-                const bool more = t + 1 < nf;
-                if (more) load_regs(p, m0, n0, t + 1, cp, ra, rb);  // in flight during compute
+                load_regs(p, m0, n0, t + 1, cp, ra, rb);  // in flight during compute
                 compute(cur, L, cp, acc);
                 if constexpr (C::S == 1) barrier();  // one buffer: all reads of it done first
-                if (more) {
-                    wait_vmcnt<0>();
-                    store_regs(nxt, tid, ra, rb);
-                }
+                wait_vmcnt<0>();
+                store_regs(nxt, tid, ra, rb);
                 wait_lgkmcnt0();
                 barrier();
             }

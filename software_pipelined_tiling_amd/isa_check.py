@@ -1,0 +1,288 @@
+"""Disassembly checks of the built K-loop kernels (gfx950 code objects in libspt.so).
+
+The pipelined loop only hides memory latency if the waits sit where the
+schedule says they do; this module reads the machine code the library
+actually ships and checks it, the counterpart of inspecting the SASS of a
+cp.async pipeline ("Pipeline GPU Kernel", Schritt 4: verify that the loads
+of the next tile are issued before the math of the current one and that the
+wait comes only where its data is needed).
+
+For each kernel it finds the steady-state loop (the backward branch whose
+body holds the most MFMAs) and reports, per loop iteration:
+
+  mfma, dma, global_loads, ds_reads, barriers   instruction counts
+  vmcnt_waits / lgkmcnt_waits                  every s_waitcnt operand
+  max_gap                                      the most non-MFMA instructions
+                                               between two MFMAs
+  scratch, acc_moves                           spill traffic and AGPR<->VGPR
+                                               copies inside the loop
+and from the code object's metadata the LDS size, VGPR/AGPR counts and spill
+counts.  `check(kernel)` turns that into pass/fail properties:
+
+  DIRECT ring (buffer_load ... lds into an S-stage ring):
+    counts     MFMAs, copies and barriers per iteration match the plan
+    vmcnt      every vmcnt wait in the loop is (S-2) x copies-per-tile: the
+               copies of younger tiles stay in flight (for S >= 3 there is
+               no vmcnt(0) in the steady state)
+    lgkmcnt    one lgkmcnt(0) per tile (before the barrier); every other
+               lgkm wait is partial, so fragment reads overlap the MFMAs
+    overlap    every copy sits in an MFMA gap of its own (none in the
+               barrier's gap) and no gap holds more than 3 fragment reads:
+               loads are interleaved with the MFMAs, not bunched
+    clean      no scratch access and no accumulator copies in the loop
+    lds        LDS size = S x stage bytes
+  SYNC: the loop drains vmcnt(0) before its first MFMA (no overlap: the
+  unpipelined reference).  REG: the tile's global loads are issued before the
+  first MFMA of the iteration and their vmcnt wait comes after the last one.
+
+Command line:  python -m software_pipelined_tiling_amd.isa_check [name-regex]
+"""
+from __future__ import annotations
+
+import dataclasses
+import os
+import re
+import struct
+import subprocess
+import sys
+import tempfile
+from typing import Dict, List, Optional
+
+LLVM = os.environ.get("ROCM_LLVM_BIN", "/opt/rocm/llvm/bin")
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+# Tile menu (BM, BN, K depth in bytes, waves along M, waves along N): the same
+# values as kTiles in csrc/spt_config.h, restated to compute expected counts.
+TILES = {1: (128, 256, 64, 2, 2), 2: (256, 256, 128, 2, 4), 3: (128, 128, 64, 2, 2),
+         4: (256, 256, 128, 2, 2), 5: (256, 256, 64, 2, 2)}
+ELT = {0: 2, 1: 2, 2: 1, 3: 4}
+VARIANTS = {1: "sync", 2: "reg", 3: "direct"}
+_CFG = re.compile(r"CfgILi(\d+)ELb(\d)ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)ELb(\d)E")
+
+
+@dataclasses.dataclass
+class Kernel:
+    name: str
+    dtype: int
+    bcol: bool
+    tile: int
+    variant: str
+    stages: int
+    exact: bool
+    instrs: List[str]
+    meta: Dict[str, int]
+
+    # expected per-tile figures from the tile geometry
+    @property
+    def geometry(self):
+        BM, BN, BKB, WM, WN = TILES[self.tile]
+        waves = WM * WN
+        fm, fn = BM // WM // 16, BN // WN // 16
+        ks = BKB // 64
+        mfma = fm * fn * ks * (4 if self.dtype == 3 else 1)
+        loads = (BM * BKB + BKB * BN) // 16 // (64 * waves)
+        stage = BM * BKB + BKB * BN
+        return dict(mfma_per_tile=mfma, loads_per_tile=loads, ks=ks, stage_bytes=stage,
+                    tiles_per_iter=1 if ks % 2 == 0 or self.variant != "direct" else 2)
+
+
+def code_objects(lib: str) -> List[bytes]:
+    """The gfx950 code objects of every offload bundle in the library's .hip_fatbin."""
+    with tempfile.TemporaryDirectory() as td:
+        fb = os.path.join(td, "fatbin")
+        subprocess.run([os.path.join(LLVM, "llvm-objcopy"), f"--dump-section=.hip_fatbin={fb}", lib,
+                        os.path.join(td, "discard")], check=True, capture_output=True)
+        data = open(fb, "rb").read()
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    out, i = [], data.find(magic)
+    while i >= 0:
+        n = struct.unpack_from("<Q", data, i + 24)[0]
+        q = i + 32
+        for _ in range(n):
+            off, size, tl = struct.unpack_from("<QQQ", data, q)
+            triple = data[q + 24:q + 24 + tl].decode()
+            q += 24 + tl
+            if triple.endswith("gfx950"):
+                out.append(data[i + off:i + off + size])
+        i = data.find(magic, i + 1)
+    return out
+
+
+def _disassemble(co: bytes) -> Dict[str, List[str]]:
+    with tempfile.NamedTemporaryFile(suffix=".co") as f:
+        f.write(co)
+        f.flush()
+        txt = subprocess.run([os.path.join(LLVM, "llvm-objdump"), "-d", "--mcpu=gfx950", f.name],
+                             check=True, capture_output=True, text=True).stdout
+    funcs: Dict[str, List[str]] = {}
+    cur = None
+    for line in txt.splitlines():
+        m = re.match(r"^[0-9a-f]+ <(\S+)>:", line)
+        if m:
+            cur = m.group(1)
+            funcs[cur] = []
+            continue
+        if cur and line.startswith("\t"):
+            body = line.strip()
+            m2 = re.search(r"//\s*([0-9A-Fa-f]+):", body)
+            addr = int(m2.group(1), 16) if m2 else -1
+            funcs[cur].append(f"{addr:x}|" + body.split("//")[0].strip())
+    return funcs
+
+
+def _metadata(co: bytes) -> Dict[str, Dict[str, int]]:
+    with tempfile.NamedTemporaryFile(suffix=".co") as f:
+        f.write(co)
+        f.flush()
+        txt = subprocess.run([os.path.join(LLVM, "llvm-readelf"), "--notes", f.name],
+                             check=True, capture_output=True, text=True).stdout
+    out: Dict[str, Dict[str, int]] = {}
+    for block in txt.split("  - .agpr_count:")[1:]:
+        name = re.search(r"\.name:\s+(\S+)", block)
+        if not name:
+            continue
+        d = {"agpr": int(block.split("\n")[0])}
+        for key, tag in (("lds", "group_segment_fixed_size"), ("scratch", "private_segment_fixed_size"),
+                         ("vgpr", "vgpr_count"), ("sgpr", "sgpr_count"), ("vgpr_spill", "vgpr_spill_count"),
+                         ("sgpr_spill", "sgpr_spill_count")):
+            m = re.search(r"\." + tag + r":\s+(\d+)", block)
+            d[key] = int(m.group(1)) if m else -1
+        out[name.group(1)] = d
+    return out
+
+
+def load(lib: Optional[str] = None) -> List[Kernel]:
+    lib = lib or os.path.join(HERE, "libspt.so")
+    ks: List[Kernel] = []
+    for co in code_objects(lib):
+        meta = _metadata(co)
+        for name, instrs in _disassemble(co).items():
+            m = _CFG.search(name)
+            if not m or "gemm_kernel" not in name:
+                continue
+            dt, bc, ti, v, s, ex, _bl = (int(x) for x in m.groups())
+            ks.append(Kernel(name, dt, bool(bc), ti, VARIANTS[v], s, bool(ex), instrs, meta.get(name, {})))
+    return ks
+
+
+def _op(ins: str) -> str:
+    return ins.split("|", 1)[1]
+
+
+def steady_loop(k: Kernel) -> List[str]:
+    """Body of the backward branch enclosing the most MFMAs."""
+    addr = [int(i.split("|")[0], 16) for i in k.instrs]
+    best: List[str] = []
+    for j, ins in enumerate(k.instrs):
+        op = _op(ins)
+        tgt = None
+        m2 = re.match(r"s_c?branch\w*\s+(\d+)$", op)
+        if m2:  # signed 16-bit target in dwords, relative to the next instruction
+            simm = int(m2.group(1))
+            simm = simm - 65536 if simm >= 32768 else simm
+            nxt = addr[j + 1] if j + 1 < len(addr) else addr[j] + 4
+            tgt = nxt + 4 * simm
+        if tgt is None or tgt > addr[j]:
+            continue
+        lo = addr.index(tgt) if tgt in addr else None
+        if lo is None:
+            continue
+        body = [_op(x) for x in k.instrs[lo:j + 1]]
+        if sum(x.startswith("v_mfma") for x in body) > sum(x.startswith("v_mfma") for x in best):
+            best = body
+    return best
+
+
+def cyclic_gaps(body: List[str]) -> List[List[str]]:
+    """The non-MFMA instructions between consecutive MFMAs of a loop body, the
+    gap across the back edge included (the body read as a cycle)."""
+    mf = [i for i, x in enumerate(body) if x.startswith("v_mfma")]
+    if not mf:
+        return []
+    rot = body[mf[0]:] + body[:mf[0]]  # starts with an MFMA
+    gaps: List[List[str]] = []
+    cur: List[str] = []
+    for x in rot[1:]:
+        if x.startswith("v_mfma"):
+            gaps.append(cur)
+            cur = []
+        else:
+            cur.append(x)
+    gaps.append(cur)  # the gap across the back edge, before the first MFMA
+    return gaps
+
+
+def loop_stats(k: Kernel) -> dict:
+    body = steady_loop(k)
+    mf = [i for i, x in enumerate(body) if x.startswith("v_mfma")]
+    cg = cyclic_gaps(body)
+    gaps = [len(g) for g in cg]
+    between = lambda pred: sum(1 for i, x in enumerate(body) if pred(x) and mf and mf[0] < i < mf[-1])
+    is_dma = lambda x: x.startswith("buffer_load") and x.rstrip().endswith("lds")
+    is_gld = lambda x: x.startswith("buffer_load") and not x.rstrip().endswith("lds")
+    is_dsr = lambda x: x.startswith("ds_read")
+    waits = [x for x in body if x.startswith("s_waitcnt")]
+    vm = [int(m.group(1)) for x in waits for m in [re.search(r"vmcnt\((\d+)\)", x)] if m]
+    lg = [int(m.group(1)) for x in waits for m in [re.search(r"lgkmcnt\((\d+)\)", x)] if m]
+    first_mfma = mf[0] if mf else 0
+    last_mfma = mf[-1] if mf else 0
+    return dict(
+        instructions=len(body), mfma=len(mf),
+        dma=sum(map(is_dma, body)), dma_between_mfma=between(is_dma),
+        global_loads=sum(map(is_gld, body)), global_loads_before_first_mfma=sum(
+            1 for i, x in enumerate(body) if is_gld(x) and i < first_mfma),
+        ds_reads=sum(map(is_dsr, body)), ds_reads_between_mfma=between(is_dsr),
+        barriers=sum(x.startswith("s_barrier") for x in body),
+        vmcnt_waits=vm, lgkmcnt_waits=lg,
+        vmcnt0_before_first_mfma=any(re.search(r"vmcnt\(0\)", x) for x in body[:first_mfma]),
+        vmcnt_after_last_mfma=[int(m.group(1)) for x in body[last_mfma:] for m in [re.search(r"vmcnt\((\d+)\)", x)] if m],
+        max_gap=max(gaps) if gaps else 0, mean_gap=round(sum(gaps) / len(gaps), 2) if gaps else 0.0,
+        dma_per_gap_max=max((sum(map(is_dma, g)) for g in cg), default=0),
+        ds_reads_per_gap_max=max((sum(map(is_dsr, g)) for g in cg), default=0),
+        dma_in_barrier_gap=sum(sum(map(is_dma, g)) for g in cg if any(x.startswith("s_barrier") for x in g)),
+        scratch=sum(x.startswith("scratch_") for x in body),
+        acc_moves=sum(x.startswith("v_accvgpr") for x in body),
+    )
+
+
+def check(k: Kernel) -> Dict[str, bool]:
+    """Pass / fail of the properties in the module docstring."""
+    g, st = k.geometry, loop_stats(k)
+    T = g["tiles_per_iter"]
+    res: Dict[str, bool] = {}
+    if k.variant == "direct":
+        res["counts"] = (st["mfma"] == T * g["mfma_per_tile"] and st["dma"] == T * g["loads_per_tile"]
+                         and st["barriers"] == T)
+        res["vmcnt"] = bool(st["vmcnt_waits"]) and all(
+            v == (k.stages - 2) * g["loads_per_tile"] for v in st["vmcnt_waits"])
+        res["lgkmcnt"] = st["lgkmcnt_waits"].count(0) == T
+        # each copy in an MFMA gap of its own, none in the gap of the barrier, fragment
+        # reads at most 3 to a gap (a 16-cycle MFMA leaves about three issue slots)
+        res["overlap"] = (st["dma_per_gap_max"] == 1 and st["dma_in_barrier_gap"] == 0
+                          and st["ds_reads_per_gap_max"] <= 3)
+        res["clean"] = st["scratch"] == 0 and st["acc_moves"] == 0
+        res["lds"] = k.meta.get("lds") == k.stages * g["stage_bytes"]
+    elif k.variant == "sync":
+        res["no_overlap"] = st["vmcnt0_before_first_mfma"]
+        res["lds"] = k.meta.get("lds") == g["stage_bytes"]
+    else:  # reg
+        res["loads_ahead"] = st["global_loads_before_first_mfma"] == st["global_loads"] > 0
+        res["wait_after_mfma"] = 0 in st["vmcnt_after_last_mfma"]
+        res["lds"] = k.meta.get("lds") == k.stages * g["stage_bytes"]
+    return res
+
+
+def report(pattern: str = ".", lib: Optional[str] = None) -> List[dict]:
+    rows = []
+    for k in load(lib):
+        if not re.search(pattern, k.name):
+            continue
+        rows.append(dict(kernel=k.name, dtype=k.dtype, bcol=k.bcol, tile=k.tile, variant=k.variant,
+                         stages=k.stages, exact=k.exact, meta=k.meta, loop=loop_stats(k), checks=check(k)))
+    return rows
+
+
+if __name__ == "__main__":
+    import json
+    for r in report(sys.argv[1] if len(sys.argv) > 1 else "."):
+        print(json.dumps(r))

@@ -1,0 +1,110 @@
+"""Disassembly checks of the shipped gfx950 kernels (no GPU needed).
+
+The machine code in libspt.so must show the schedule the ring promises:
+copies of later tiles issued between the MFMAs of the current one, the
+steady-state vmcnt wait leaving (S-2) tiles of copies in flight, partial
+lgkmcnt waits for the LDS -> VGPR fragment pipeline, one barrier per K tile,
+no spills or accumulator copies inside the loop, and the LDS ring size of the
+plan ("Pipeline GPU Kernel", Schritt 4: check in the generated code that the
+next tile's loads are in flight during the math of the current one).
+"""
+import os
+import shutil
+
+import pytest
+
+from software_pipelined_tiling_amd import isa_check as X
+
+pytestmark = pytest.mark.skipif(not os.path.exists(os.path.join(X.LLVM, "llvm-objdump")),
+                                reason="ROCm llvm-objdump not installed")
+
+
+@pytest.fixture(scope="module")
+def kernels(built_lib):
+    ks = X.load()
+    assert ks, "no gemm kernels found in libspt.so"
+    return ks
+
+
+def pick(ks, **kw):
+    out = [k for k in ks if all(getattr(k, a) == v for a, v in kw.items())]
+    assert out, kw
+    return out
+
+
+def test_every_built_entry_is_in_the_binary(kernels):
+    # 8 tables (element type x B layout) of 34: SYNC, REG 1/2 and DIRECT 2 on every
+    # tile, DIRECT 3/4 where the ring fits in LDS, exact-fit forms of tiles 1, 2, 4, 5
+    assert len(kernels) == 8 * 34
+    assert {k.tile for k in kernels} == {1, 2, 3, 4, 5}
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_fp16_bf16_exact_rings_pass_every_check(kernels, dtype):
+    for k in pick(kernels, dtype=dtype, variant="direct", exact=True):
+        res = X.check(k)
+        assert all(res.values()), (k.name, res, X.loop_stats(k))
+
+
+def test_headline_kernel_schedule(kernels):
+    """256 x 256, 2-stage ring, fp16, row-major B, exact fit: 128 MFMAs and 16
+    copies per K tile, one barrier, the copies one per MFMA gap, the wait before
+    the barrier drains only the tile about to be read (vmcnt(0) with 2 stages)."""
+    (k,) = pick(kernels, dtype=0, bcol=False, tile=4, variant="direct", stages=2, exact=True)
+    st = X.loop_stats(k)
+    assert (st["mfma"], st["dma"], st["barriers"]) == (128, 16, 1)
+    assert st["vmcnt_waits"] == [0]
+    assert st["dma_per_gap_max"] == 1 and st["dma_in_barrier_gap"] == 0
+    assert st["scratch"] == 0 and st["acc_moves"] == 0
+    assert k.meta["lds"] == 131072 and k.meta["agpr"] == 256 and k.meta["vgpr_spill"] == 0
+
+
+@pytest.mark.parametrize("tile,stages,loads", [(5, 3, 8), (5, 4, 8), (1, 3, 6), (1, 4, 6), (3, 3, 4)])
+def test_deep_rings_keep_copies_in_flight(kernels, tile, stages, loads):
+    """With S >= 3 the steady loop never waits for all copies: every vmcnt wait
+    leaves the (S-2) younger tiles' copies in flight."""
+    # (the general 256 x 256 kernels carry edge and tail code and spill in their loop;
+    # scratch loads count in vmcnt too, so only their exact-fit forms are checked here)
+    for k in pick(kernels, dtype=0, tile=tile, variant="direct", stages=stages):
+        if tile in (4, 5) and not k.exact:
+            continue
+        st = X.loop_stats(k)
+        assert st["vmcnt_waits"] and all(v == (stages - 2) * loads for v in st["vmcnt_waits"]), st
+        assert 0 not in st["vmcnt_waits"]
+
+
+def test_every_ring_has_the_planned_structure(kernels):
+    """Counts (MFMAs, copies, barriers per loop iteration) and the LDS ring size
+    hold for every DIRECT kernel of every element type and layout."""
+    for k in pick(kernels, variant="direct"):
+        res = X.check(k)
+        assert res["counts"] and res["lds"], (k.name, res, X.loop_stats(k))
+
+
+def test_small_tile_rings_are_clean(kernels):
+    """Tiles with two waves per SIMD (1, 2, 3) keep accumulators in VGPRs: no
+    spills or register copies in any of their ring loops, general or exact."""
+    for k in kernels:
+        if k.variant == "direct" and k.tile in (1, 2, 3) and k.stages <= 3:
+            st = X.loop_stats(k)
+            assert st["scratch"] == 0 and st["acc_moves"] == 0, (k.name, st)
+
+
+def test_sync_loop_does_not_overlap(kernels):
+    """The unpipelined reference drains its loads before its first MFMA."""
+    for k in pick(kernels, variant="sync"):
+        res = X.check(k)
+        assert res["no_overlap"] and res["lds"], (k.name, res)
+
+
+def test_register_staged_prefetch_overlaps(kernels):
+    """REG issues tile t+1's global loads before tile t's first MFMA and waits
+    for them only after its last one."""
+    for k in pick(kernels, variant="reg"):
+        res = X.check(k)
+        assert all(res.values()), (k.name, res, X.loop_stats(k))
+
+
+def test_cyclic_gaps_on_a_toy_loop():
+    body = ["s_barrier", "v_mfma a", "buffer_load x lds", "v_mfma b", "ds_read_b128 y", "ds_read_b128 z"]
+    assert X.cyclic_gaps(body) == [["buffer_load x lds"], ["ds_read_b128 y", "ds_read_b128 z", "s_barrier"]]
