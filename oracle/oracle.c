@@ -233,3 +233,26 @@ int oracle_max_threads(void)
 {
     return set_threads(0);
 }
+
+/*
+ * The streaming pipeline of "Hiding Memory Latency in CUDA: Asynchronous
+ * Loads and Software Pipelines" (section 8, the minimal example): every
+ * element of a float vector is scaled by two,
+ *
+ *        y[i] = 2 * x[i]      (0 <= i < n),
+ *
+ * in float, as the page computes it.  Here each value is decoded exactly to
+ * double, doubled there and rounded once back to float; doubling is exact in
+ * both formats (overflow to infinity and NaN included), so this is the plain
+ * definition.  x and y are raw binary32 bit patterns.  n = 0 writes nothing.
+ */
+int oracle_scale_by_two(int64_t n, const uint32_t* x, uint32_t* y)
+{
+    if (n < 0 || (n > 0 && (!x || !y))) return -1;
+    for (int64_t i = 0; i < n; ++i) {
+        const double v = 2.0 * oracle_f32_to_f64(x[i]);
+        const float f = (float)v;
+        memcpy(&y[i], &f, sizeof f);
+    }
+    return 0;
+}

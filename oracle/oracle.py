@@ -56,6 +56,7 @@ def lib():
         L.oracle_gemm_int8_entries.argtypes = [i64, vp, i64, vp, i64, i32, i64, vp, vp, vp, i32]
         L.oracle_decode_array.argtypes = [i32, vp, i64, vp]
         L.oracle_max_threads.argtypes = []
+        L.oracle_scale_by_two.argtypes = [i64, vp, vp]
         for f in ("oracle_gemm_float", "oracle_gemm_float_entries", "oracle_gemm_int8",
                   "oracle_gemm_int8_entries", "oracle_decode_array", "oracle_max_threads"):
             getattr(L, f).restype = i32
@@ -148,6 +149,15 @@ def gemm_entries(A: np.ndarray, B: np.ndarray, dtype: str, rows, cols, *, b_col:
                                            int(b_col), r.size, _ptr(r), _ptr(c), _ptr(out),
                                            threads))
     return out
+
+
+def scale_by_two(x: np.ndarray) -> np.ndarray:
+    """y = 2 * x elementwise for a float32 vector ("Hiding Memory Latency ...",
+    section 8); returns a new float32 array."""
+    xb = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    y = np.empty_like(xb)
+    _check(lib().oracle_scale_by_two(xb.size, _ptr(xb), _ptr(y)))
+    return y.view(np.float32)
 
 
 def max_threads() -> int:
