@@ -16,6 +16,9 @@ Besides the headline value it reports, in the same line:
                 headline workload, the unpipelined one included
   workloads     int8 4096^3 (B column-major), bf16 8192^2 x K low-K sweep
                 (with HBM GB/s), bf16 4000x3000x1000 ragged, fp16 256^3
+  streaming     y = 2x through the S-stage ring: the pages' demonstration
+                (2^20 floats, one block, 3 stages) and 2^28 floats over many
+                blocks, each with the unpipelined S = 1 loop beside it
   power         socket power and GFX clocks sampled with amd-smi while the
                 headline kernel runs back to back for a few seconds, and the
                 dense peak at that clock (context for the roofline fraction)
@@ -130,6 +133,40 @@ def traffic_from_profile(kernel_sha: str):
     if d.get("kernel_source_sha") != kernel_sha:
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+def stream_bench(steps: int, warmup: int):
+    """y = 2x ("Hiding Memory Latency ...", section 8) through spt_scale_by_two:
+    8 bytes per element (one read, one write), HBM-bound."""
+    import torch
+    import software_pipelined_tiling_amd as spt
+    out = {}
+    stream = torch.cuda.current_stream()
+    for name, n, blocks in (("pages demo: 2^20 floats, 1 block", 1 << 20, 1),
+                            ("2^28 floats, library blocks", 1 << 28, 0)):
+        x = (torch.arange(n, device="cuda", dtype=torch.int64) % 113).to(torch.float32) * 0.25
+        y = torch.empty_like(x)
+        res = {}
+        for s in (1, 2, 3, 4):
+            def call():
+                return spt.spt_scale_by_two(n, x.data_ptr(), y.data_ptr(), s, blocks, stream.cuda_stream)
+            if call() != 0:
+                raise RuntimeError(spt.spt_last_error())
+            for _ in range(warmup):
+                call()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                call()
+            e1.record(stream)
+            e1.synchronize()
+            us = e0.elapsed_time(e1) / steps * 1e3
+            res[f"S{s}"] = {"us": round(us, 2), "gbs": round(8 * n / us / 1e3, 1),
+                            "pct_of_hbm": round(100 * 8 * n / us / 1e3 / HBM_GBS, 1)}
+        res["speedup_S3_vs_S1"] = round(res["S1"]["us"] / res["S3"]["us"], 3)
+        out[name] = res
+        del x, y
+    return out
 
 
 def sample_power(prob: "Problem", seconds: float):
@@ -309,6 +346,9 @@ def main():
                               "speedup_vs_unpipelined": round(t1 / t, 3)}
             del p
         out["workloads"] = extra
+
+        if not args.only_workload:
+            out["streaming"] = stream_bench(steps, 20)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(I.W_F16_4096, args.cpu_budget)

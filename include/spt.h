@@ -174,6 +174,24 @@ int spt_plan(int dtype, int64_t M, int64_t N, int64_t K,
              int b_layout, int variant, int stages, int tile_id,
              spt_plan_info* out);
 
+/*
+ * y[i] = 2 * x[i] for 0 <= i < n: the streaming pipeline of "Hiding Memory
+ * Latency ...", section 8 (the minimal working example) and section 9, on
+ * gfx950.  x and y are DEVICE pointers to float32 arrays owned by the caller,
+ * 16-byte aligned (SPT_ERR_MISALIGNED otherwise); y may be x itself (in
+ * place) but must not overlap it otherwise (SPT_ERR_INVALID).  Tiles of 1024
+ * elements are staged global -> LDS through a ring of `stages` stages (1 =
+ * the synchronous loop, 2..4 = asynchronous copies; 0 = 3, the page's
+ * choice); each of `blocks` workgroups of 256 threads walks its own stream of
+ * tiles (0 = the library's choice: one per tile up to 2048; 1 = the page's
+ * single-block demonstration; more blocks than tiles are not launched).
+ * Every result is exact (doubling is exact in float).  n = 0 returns SPT_OK
+ * without launching; n < 0, stages outside 0..4 or blocks < 0 give
+ * SPT_ERR_INVALID; n > 2^40 gives SPT_ERR_UNSUPPORTED.  Asynchronous on
+ * `stream`, like spt_gemm.
+ */
+int spt_scale_by_two(int64_t n, const void* x, void* y, int stages, int blocks, void* stream);
+
 /* Static string naming a status code. */
 const char* spt_status_string(int status);
 

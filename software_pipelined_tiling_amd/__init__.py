@@ -15,7 +15,7 @@ import os
 
 __all__ = [
     "spt_gemm", "spt_gemm_ex", "spt_plan", "spt_status_string", "spt_last_error", "spt_version",
-    "gemm", "plan", "SptError", "PlanInfo", "lib_path",
+    "spt_scale_by_two", "gemm", "plan", "scale_by_two", "SptError", "PlanInfo", "lib_path",
     "F16", "BF16", "I8", "F32", "ROW", "COL", "VARIANT_AUTO", "VARIANT_SYNC", "VARIANT_REG",
     "VARIANT_DIRECT", "TILE_AUTO", "TILE_128x256", "TILE_256x256", "TILE_128x128", "TILE_256x256_4W",
     "TILE_256x256_4W_K64B",
@@ -86,6 +86,8 @@ def _load():
         L.spt_last_error.restype = ctypes.c_char_p
         L.spt_version.argtypes = []
         L.spt_version.restype = i32
+        L.spt_scale_by_two.argtypes = [i64, vp, vp, i32, i32, vp]
+        L.spt_scale_by_two.restype = i32
         _lib = L
     return _lib
 
@@ -112,6 +114,10 @@ def spt_plan(dtype, M, N, K, b_layout=ROW, variant=VARIANT_AUTO, stages=0, tile_
     info = PlanInfo()
     rc = _load().spt_plan(dtype, M, N, K, b_layout, variant, stages, tile_id, ctypes.byref(info))
     return rc, info
+
+
+def spt_scale_by_two(n, x, y, stages=0, blocks=0, stream=0) -> int:
+    return _load().spt_scale_by_two(n, x, y, stages, blocks, stream)
 
 
 def spt_status_string(status: int) -> str:
@@ -180,4 +186,22 @@ def gemm(A, B, out=None, *, b_layout: str = "row", variant: str = "auto", stages
                      tile)
     if rc != SPT_OK:
         raise SptError(rc, "spt_gemm_ex")
+    return out
+
+
+def scale_by_two(x, out=None, *, stages: int = 0, blocks: int = 0, stream=None):
+    """out = 2 * x for a contiguous float32 torch tensor on the GPU, through
+    ``spt_scale_by_two`` (out may be x itself)."""
+    import torch
+    if x.dtype != torch.float32 or not x.is_contiguous():
+        raise TypeError("x must be a contiguous float32 tensor")
+    if out is None:
+        out = torch.empty_like(x)
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.numel() != x.numel():
+        raise ValueError("out must be a contiguous float32 tensor of x's size")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    rc = spt_scale_by_two(x.numel(), x.data_ptr(), out.data_ptr(), stages, blocks, stream)
+    if rc != SPT_OK:
+        raise SptError(rc, "spt_scale_by_two")
     return out

@@ -206,9 +206,41 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     return SPT_OK;
 }
 
+// The streaming pipeline: validation, then one launch.
+static int scale_by_two_impl(int64_t n, const void* x, void* y, int stages, int blocks, void* stream)
+{
+    if (n < 0) return fail(SPT_ERR_INVALID, "negative n");
+    if (stages < 0 || stages > 4) return fail(SPT_ERR_INVALID, "stages %d not in 0..4", stages);
+    if (blocks < 0) return fail(SPT_ERR_INVALID, "negative blocks");
+    if (n > (int64_t)1 << 40) return fail(SPT_ERR_UNSUPPORTED, "n above 2^40");
+    if (n == 0) return SPT_OK;
+    if (!x || !y) return fail(SPT_ERR_INVALID, "x or y is null");
+    const uintptr_t xa = (uintptr_t)x, ya = (uintptr_t)y;
+    const uintptr_t bytes = (uintptr_t)n * 4;
+    if (xa != ya && xa < ya + bytes && ya < xa + bytes)
+        return fail(SPT_ERR_INVALID, "x and y overlap without being the same array");
+    if (xa % 16 || ya % 16) return fail(SPT_ERR_MISALIGNED, "x or y not 16-byte aligned");
+    if (xa >> 47 || ya >> 47 || xa < 65536 || ya < 65536)
+        return fail(SPT_ERR_UNSUPPORTED, "x or y outside the device address range of buffer descriptors");
+    const int64_t tiles = (n + 1023) / 1024;
+    // default: the pages' three stages; one block per tile up to 8 per CU
+    const int s = stages == 0 ? 3 : stages;
+    int64_t g = blocks == 0 ? (tiles < 2048 ? tiles : 2048) : (blocks < tiles ? blocks : tiles);
+    const hipError_t err = launch_scale_by_two(x, y, n, s, (unsigned)g, (hipStream_t)stream);
+    if (err != hipSuccess) return fail(SPT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(err));
+    g_last_error[0] = 0;
+    return SPT_OK;
+}
+
 }  // namespace spt
 
 extern "C" {
+
+int spt_scale_by_two(int64_t n, const void* x, void* y, int stages, int blocks, void* stream)
+{
+    return spt::scale_by_two_impl(n, x, y, stages, blocks, stream);
+}
+
 
 int spt_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
              void* C, int64_t ldc, int dtype, void* stream)

@@ -32,6 +32,9 @@ KernelTable kernels_i8_col();
 KernelTable kernels_f32_row();
 KernelTable kernels_f32_col();
 
+// The streaming pipeline y = 2 x (spt_stream.hip); arguments already validated.
+hipError_t launch_scale_by_two(const void* x, void* y, int64_t n, int stages, unsigned blocks, hipStream_t stream);
+
 // nullptr when that combination is not built.  exact = 1 asks for the
 // instantiation that assumes M, N, K are multiples of the tile.
 const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int stages, int exact);

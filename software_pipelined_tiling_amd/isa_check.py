@@ -35,6 +35,12 @@ counts.  `check(kernel)` turns that into pass/fail properties:
   unpipelined reference).  REG: the tile's global loads are issued before the
   first MFMA of the iteration and their vmcnt wait comes after the last one.
 
+The streaming kernel (y = 2x, "Hiding Memory Latency ...", section 8) is
+checked too (`check_stream`): per loop iteration one copy, one store and one
+barrier, and the steady wait vmcnt(2S-3) (S >= 2: copies and stores share
+the in-order counter; the S-1 younger copies and their stores stay in
+flight); S = 1 waits for everything and has two barriers.
+
 Command line:  python -m software_pipelined_tiling_amd.isa_check [name-regex]
 """
 from __future__ import annotations
@@ -165,30 +171,79 @@ def load(lib: Optional[str] = None) -> List[Kernel]:
     return ks
 
 
+@dataclasses.dataclass
+class StreamKernel:
+    name: str
+    stages: int
+    instrs: List[str]
+    meta: Dict[str, int]
+
+
+def load_stream(lib: Optional[str] = None) -> List[StreamKernel]:
+    lib = lib or os.path.join(HERE, "libspt.so")
+    out: List[StreamKernel] = []
+    for co in code_objects(lib):
+        meta = _metadata(co)
+        for name, instrs in _disassemble(co).items():
+            m = re.search(r"scale_by_two_kernelILi(\d+)E", name)
+            if m:
+                out.append(StreamKernel(name, int(m.group(1)), instrs, meta.get(name, {})))
+    return out
+
+
+def check_stream(k: StreamKernel) -> Dict[str, bool]:
+    # the ring loop: the shortest loop body that holds a copy and a barrier
+    cands = [b for b in loop_regions(k) if _count_copies(b) and any(x.startswith("s_barrier") for x in b)]
+    body = min(cands, key=len) if cands else []
+    dma = sum(x.startswith("buffer_load") and x.rstrip().endswith("lds") for x in body)
+    st = sum(x.startswith("buffer_store") for x in body)
+    bar = sum(x.startswith("s_barrier") for x in body)
+    vm = [int(m.group(1)) for x in body for m in [re.search(r"vmcnt\((\d+)\)", x)] if m]
+    S = k.stages
+    res = {"counts": dma == 1 and st == 1 and bar == (2 if S == 1 else 1),
+           "vmcnt": vm == ([0] if S == 1 else [2 * S - 3]),
+           "lds": k.meta.get("lds") == S * 4096,
+           "clean": not any(x.startswith("scratch_") for x in body)}
+    return res
+
+
 def _op(ins: str) -> str:
     return ins.split("|", 1)[1]
 
 
-def steady_loop(k: Kernel) -> List[str]:
-    """Body of the backward branch enclosing the most MFMAs."""
+def _count_mfma(body: List[str]) -> int:
+    return sum(x.startswith("v_mfma") for x in body)
+
+
+def _count_copies(body: List[str]) -> int:
+    return sum(x.startswith("buffer_load") and x.rstrip().endswith("lds") for x in body)
+
+
+def loop_regions(k) -> List[List[str]]:
+    """Instructions from the target of every backward branch to the branch
+    (the body of a loop, as laid out)."""
     addr = [int(i.split("|")[0], 16) for i in k.instrs]
-    best: List[str] = []
+    pos = {a: n for n, a in enumerate(addr)}
+    out: List[List[str]] = []
     for j, ins in enumerate(k.instrs):
-        op = _op(ins)
-        tgt = None
-        m2 = re.match(r"s_c?branch\w*\s+(\d+)$", op)
-        if m2:  # signed 16-bit target in dwords, relative to the next instruction
-            simm = int(m2.group(1))
-            simm = simm - 65536 if simm >= 32768 else simm
-            nxt = addr[j + 1] if j + 1 < len(addr) else addr[j] + 4
-            tgt = nxt + 4 * simm
-        if tgt is None or tgt > addr[j]:
+        m2 = re.match(r"s_c?branch\w*\s+(\d+)$", _op(ins))
+        if not m2:
             continue
-        lo = addr.index(tgt) if tgt in addr else None
-        if lo is None:
-            continue
-        body = [_op(x) for x in k.instrs[lo:j + 1]]
-        if sum(x.startswith("v_mfma") for x in body) > sum(x.startswith("v_mfma") for x in best):
+        simm = int(m2.group(1))  # signed 16-bit target in dwords, relative to the next instruction
+        simm = simm - 65536 if simm >= 32768 else simm
+        nxt = addr[j + 1] if j + 1 < len(addr) else addr[j] + 4
+        tgt = nxt + 4 * simm
+        if tgt <= addr[j] and tgt in pos:
+            out.append([_op(x) for x in k.instrs[pos[tgt]:j + 1]])
+    return out
+
+
+def steady_loop(k, key=_count_mfma) -> List[str]:
+    """The loop body holding the most MFMAs (or the most of what `key` counts);
+    among equals the shortest."""
+    best: List[str] = []
+    for body in loop_regions(k):
+        if key(body) > key(best) or (key(body) == key(best) > 0 and len(body) < len(best)):
             best = body
     return best
 

@@ -27,7 +27,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert names == sorted(["spt_gemm", "spt_gemm_ex", "spt_plan", "spt_status_string",
-                            "spt_last_error", "spt_version"])
+                            "spt_last_error", "spt_version", "spt_scale_by_two"])
     for n in names:
         assert hasattr(L, n), n
 
@@ -132,3 +132,24 @@ def test_pages_tile_plan(L):
     assert (pi.a_copies_per_thread, pi.b_copies_per_thread) == (2, 4)
     assert pi.wg_per_cu_lds == 2 and pi.steady_vmcnt == 6
     assert pi.grid == 512 and pi.k_tiles == 128
+
+
+# ---- the streaming pipeline y = 2x: validation before any HIP call -----------
+X0, Y0 = 0x100000, 0x200000   # fake, aligned, far apart
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), -1), (dict(stages=5), -1), (dict(stages=-1), -1), (dict(blocks=-2), -1),
+    (dict(x=0), -1), (dict(y=0), -1), (dict(y=X0 + 4), -1),          # partial overlap
+    (dict(x=X0 + 4, y=X0 + 4 + (1 << 20)), -3), (dict(y=Y0 + 8), -3),  # misaligned
+    (dict(x=0x8000, y=0x9000 + (1 << 20)), -2), (dict(y=1 << 47), -2), (dict(n=(1 << 40) + 1), -2),
+])
+def test_scale_by_two_validation(L, kw, status):
+    a = dict(n=1000, x=X0, y=Y0, stages=0, blocks=0)
+    a.update(kw)
+    assert spt.spt_scale_by_two(a["n"], a["x"], a["y"], a["stages"], a["blocks"], 0) == status
+    assert spt.spt_last_error() != ""
+
+
+def test_scale_by_two_empty_is_ok(L):
+    assert spt.spt_scale_by_two(0, 0, 0, 0, 0, 0) == 0

@@ -108,3 +108,14 @@ def test_register_staged_prefetch_overlaps(kernels):
 def test_cyclic_gaps_on_a_toy_loop():
     body = ["s_barrier", "v_mfma a", "buffer_load x lds", "v_mfma b", "ds_read_b128 y", "ds_read_b128 z"]
     assert X.cyclic_gaps(body) == [["buffer_load x lds"], ["ds_read_b128 y", "ds_read_b128 z", "s_barrier"]]
+
+
+def test_streaming_ring_schedule(built_lib):
+    """y = 2x ("Hiding Memory Latency ...", section 8): one copy, one store and one
+    barrier per tile, and the steady wait vmcnt(2S-3) that leaves the S-1 younger
+    copies and their stores in flight (S = 1: vmcnt(0) and two barriers)."""
+    ks = X.load_stream()
+    assert sorted(k.stages for k in ks) == [1, 2, 3, 4]
+    for k in ks:
+        res = X.check_stream(k)
+        assert all(res.values()), (k.name, res)
