@@ -143,6 +143,7 @@ def stream_bench(steps: int, warmup: int):
     out = {}
     stream = torch.cuda.current_stream()
     for name, n, blocks in (("pages demo: 2^20 floats, 1 block", 1 << 20, 1),
+                            ("2^28 floats, 256 blocks (one per CU)", 1 << 28, 256),
                             ("2^28 floats, library blocks", 1 << 28, 0)):
         x = (torch.arange(n, device="cuda", dtype=torch.int64) % 113).to(torch.float32) * 0.25
         y = torch.empty_like(x)
@@ -164,6 +165,19 @@ def stream_bench(steps: int, warmup: int):
             res[f"S{s}"] = {"us": round(us, 2), "gbs": round(8 * n / us / 1e3, 1),
                             "pct_of_hbm": round(100 * 8 * n / us / 1e3 / HBM_GBS, 1)}
         res["speedup_S3_vs_S1"] = round(res["S1"]["us"] / res["S3"]["us"], 3)
+        if n == 1 << 28 and blocks == 0:  # context: torch's own elementwise multiply
+            t = torch.empty_like(x)
+            for _ in range(warmup):
+                torch.mul(x, 2.0, out=t)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                torch.mul(x, 2.0, out=t)
+            e1.record(stream)
+            e1.synchronize()
+            us = e0.elapsed_time(e1) / steps * 1e3
+            res["torch_mul_reference"] = {"us": round(us, 2), "gbs": round(8 * n / us / 1e3, 1)}
+            del t
         out[name] = res
         del x, y
     return out

@@ -223,9 +223,12 @@ static int scale_by_two_impl(int64_t n, const void* x, void* y, int stages, int 
     if (xa >> 47 || ya >> 47 || xa < 65536 || ya < 65536)
         return fail(SPT_ERR_UNSUPPORTED, "x or y outside the device address range of buffer descriptors");
     const int64_t tiles = (n + 1023) / 1024;
-    // default: the pages' three stages; one block per tile up to 8 per CU
+    // default: the pages' three stages.  Blocks (measured on MI355X at 2^28
+    // floats): a ring of 3-4 stages keeps enough copies in flight with two
+    // blocks per CU; S <= 2 needs about four to hide the same latency.
     const int s = stages == 0 ? 3 : stages;
-    int64_t g = blocks == 0 ? (tiles < 2048 ? tiles : 2048) : (blocks < tiles ? blocks : tiles);
+    const int64_t want = blocks != 0 ? blocks : (s >= 3 ? 512 : 1024);
+    const int64_t g = want < tiles ? want : tiles;
     const hipError_t err = launch_scale_by_two(x, y, n, s, (unsigned)g, (hipStream_t)stream);
     if (err != hipSuccess) return fail(SPT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(err));
     g_last_error[0] = 0;
