@@ -22,6 +22,8 @@ Besides the headline value it reports, in the same line:
   power         socket power and GFX clocks sampled with amd-smi while the
                 headline kernel runs back to back for a few seconds, and the
                 dense peak at that clock (context for the roofline fraction)
+  mfma_ceiling  the rate MFMAs alone sustain with the headline's operand data
+                under the power limit (spt_probe_mfma), and value / that rate
 """
 from __future__ import annotations
 
@@ -183,6 +185,40 @@ def stream_bench(steps: int, warmup: int):
     return out
 
 
+def mfma_ceiling(prob: "Problem", seconds: float):
+    """Sustained rate of MFMAs alone (spt_probe_mfma, no memory traffic in the
+    loop) with the headline's own A matrix as operand data: the compute roof
+    the power limit leaves for this data (context for the roofline fraction)."""
+    import torch
+    import software_pipelined_tiling_amd as spt
+    stream = torch.cuda.current_stream()
+    sink = torch.empty(65536, dtype=torch.float32, device="cuda")
+    nbytes = prob.dA.numel() * prob.dA.element_size()
+    iters = 2000  # ~1 ms per launch
+    code = spt.DTYPE_CODES[prob.w.dtype]
+
+    def launch():
+        return spt.spt_probe_mfma(code, prob.dA.data_ptr(), nbytes, iters, sink.data_ptr(), stream.cuda_stream)
+    if launch() != 0:
+        return None
+    for _ in range(100):
+        launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 0
+    t0 = time.perf_counter()
+    e0.record(stream)
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            launch()
+        torch.cuda.synchronize()
+        n += 50
+    e1.record(stream)
+    e1.synchronize()
+    ops = 256 * 4 * 64 * iters * (32768 if prob.w.dtype == "i8" else 16384) * n
+    return round(ops / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+
+
 def sample_power(prob: "Problem", seconds: float):
     """Run the headline call back to back for `seconds` while amd-smi samples
     socket power and the GFX (XCD) clocks; None when amd-smi is unavailable."""
@@ -320,6 +356,11 @@ def main():
 
     if not args.only_headline and not args.no_power:
         out["power"] = sample_power(head, args.power_seconds)
+        ceil = mfma_ceiling(head, 2.0)
+        if ceil:
+            out["mfma_ceiling"] = {"tflops": ceil, "value_over_ceiling": round(tflops / ceil, 4),
+                                   "what": "spt_probe_mfma: 16x16x32 fp16 MFMAs alone, operands = the headline's "
+                                           "A matrix, one wave per SIMD on every CU, sustained 2 s"}
 
     if args.only_workload:
         args.no_sweep = True

@@ -19,7 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = [f"spt_kernels_{dt}_{lay}.hip" for dt in ("f16", "bf16", "i8", "f32") for lay in ("row", "col")]
-SOURCES += ["spt_stream.hip", "spt_api.cpp"]
+SOURCES += ["spt_stream.hip", "spt_probe.hip", "spt_api.cpp"]
 HEADERS = ["spt_kernel.hpp", "spt_instances.hpp", "spt_registry.h", "spt_config.h"]
 
 # Packed-fp32 VALU instructions are disabled for all device code (-packed-fp32-ops).

@@ -8,6 +8,7 @@
 #include <cstring>
 
 #include "../../include/spt.h"
+#include "../../include/spt_probe.h"
 #include "spt_config.h"
 #include "spt_registry.h"
 
@@ -235,9 +236,28 @@ static int scale_by_two_impl(int64_t n, const void* x, void* y, int stages, int 
     return SPT_OK;
 }
 
+static int mfma_probe_impl(int dtype, const void* ops, int64_t bytes, int64_t iters, void* sink, void* stream)
+{
+    if (dtype != DT_F16 && dtype != DT_BF16 && dtype != DT_I8)
+        return fail(SPT_ERR_INVALID, "dtype %d: the probe covers f16, bf16 and i8", dtype);
+    if (!ops || !sink) return fail(SPT_ERR_INVALID, "operands or sink is null");
+    if (bytes < 16 || iters < 0) return fail(SPT_ERR_INVALID, "fewer than 16 operand bytes or negative iters");
+    if ((uintptr_t)ops % 16) return fail(SPT_ERR_MISALIGNED, "operands not 16-byte aligned");
+    const hipError_t err = launch_mfma_probe(dtype, ops, bytes / 16, iters, (float*)sink, (hipStream_t)stream);
+    if (err != hipSuccess) return fail(SPT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(err));
+    g_last_error[0] = 0;
+    return SPT_OK;
+}
+
 }  // namespace spt
 
 extern "C" {
+
+int spt_probe_mfma(int dtype, const void* operands, int64_t operand_bytes, int64_t iters, void* sink, void* stream)
+{
+    return spt::mfma_probe_impl(dtype, operands, operand_bytes, iters, sink, stream);
+}
+
 
 int spt_scale_by_two(int64_t n, const void* x, void* y, int stages, int blocks, void* stream)
 {

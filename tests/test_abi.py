@@ -19,7 +19,8 @@ def L(built_lib):
 
 
 def declared_functions():
-    txt = open(os.path.join(ROOT, "include", "spt.h")).read()
+    inc = os.path.join(ROOT, "include")
+    txt = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(spt_\w+)\s*\(", txt, flags=re.M)))
 
@@ -27,7 +28,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert names == sorted(["spt_gemm", "spt_gemm_ex", "spt_plan", "spt_status_string",
-                            "spt_last_error", "spt_version", "spt_scale_by_two"])
+                            "spt_last_error", "spt_version", "spt_scale_by_two", "spt_probe_mfma"])
     for n in names:
         assert hasattr(L, n), n
 
@@ -153,3 +154,12 @@ def test_scale_by_two_validation(L, kw, status):
 
 def test_scale_by_two_empty_is_ok(L):
     assert spt.spt_scale_by_two(0, 0, 0, 0, 0, 0) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((3, X0, 1024, 1, Y0), -1), ((0, 0, 1024, 1, Y0), -1), ((0, X0, 1024, 1, 0), -1), ((0, X0, 8, 1, Y0), -1),
+    ((0, X0, 1024, -1, Y0), -1), ((0, X0 + 4, 1024, 1, Y0), -3),
+])
+def test_probe_validation(L, args, status):
+    assert spt.spt_probe_mfma(*args, 0) == status
+    assert spt.spt_last_error() != ""
