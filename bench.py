@@ -46,10 +46,16 @@ TILES = (1, 2, 3, 4, 5)
 FLOP_PER_CLK = {"f16": 256 * 4096, "bf16": 256 * 4096, "i8": 256 * 8192}  # dense MFMA, whole chip
 
 
+# The sources that define the headline's GEMM kernel (its template, tile menu,
+# instantiation and translation unit): a committed counter summary applies
+# only while these are unchanged.
+KERNEL_SOURCES = ("spt_kernel.hpp", "spt_config.h", "spt_instances.hpp", "spt_registry.h", "spt_kernels_f16_row.hip")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "software_pipelined_tiling_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in KERNEL_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -219,6 +225,20 @@ def mfma_ceiling(prob: "Problem", seconds: float):
     return round(ops / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
 
 
+def mfma_ceilings(prob: "Problem", seconds: float):
+    """mfma_ceiling with the headline's data, and with all-zero operands (the
+    same instructions with no operand bits switching)."""
+    import torch
+    rate = mfma_ceiling(prob, seconds)
+    keep = prob.dA
+    prob.dA = torch.zeros_like(keep)
+    try:
+        rate0 = mfma_ceiling(prob, seconds)
+    finally:
+        prob.dA = keep
+    return rate, rate0
+
+
 def sample_power(prob: "Problem", seconds: float):
     """Run the headline call back to back for `seconds` while amd-smi samples
     socket power and the GFX (XCD) clocks; None when amd-smi is unavailable."""
@@ -356,11 +376,13 @@ def main():
 
     if not args.only_headline and not args.no_power:
         out["power"] = sample_power(head, args.power_seconds)
-        ceil = mfma_ceiling(head, 2.0)
+        ceil, ceil0 = mfma_ceilings(head, 2.0)
         if ceil:
             out["mfma_ceiling"] = {"tflops": ceil, "value_over_ceiling": round(tflops / ceil, 4),
+                                   "zero_operands_tflops": ceil0,
                                    "what": "spt_probe_mfma: 16x16x32 fp16 MFMAs alone, operands = the headline's "
-                                           "A matrix, one wave per SIMD on every CU, sustained 2 s"}
+                                           "A matrix (and, for comparison, zeros), one wave per SIMD on every CU, "
+                                           "sustained 2 s each"}
 
     if args.only_workload:
         args.no_sweep = True
