@@ -163,3 +163,11 @@ def test_scale_by_two_empty_is_ok(L):
 def test_probe_validation(L, args, status):
     assert spt.spt_probe_mfma(*args, 0) == status
     assert spt.spt_last_error() != ""
+
+
+def test_panel_above_2gib_is_refused(L):
+    """A 256-row panel of A with a 2^22-element fp16 pitch is 2 GiB of buffer
+    offsets: refused before any launch."""
+    K = 1 << 22
+    assert ex(M=256, N=256, K=K, lda=K, tile=spt.TILE_256x256_4W) == -2
+    assert "2 GiB" in spt.spt_last_error()

@@ -287,3 +287,37 @@ def test_full_bf16_lowk(oracle_mod, K):
 @pytest.mark.parametrize("variant,stages", [("auto", 0), ("reg", 2), ("sync", 1)])
 def test_full_bf16_ragged(oracle_mod, variant, stages):
     sampled(oracle_mod, I.W_BF16_RAGGED, variant, stages)
+
+
+# ---- maximum sizes ------------------------------------------------------------
+@pytest.mark.parametrize("b_col", [False, True])
+def test_int8_max_k_extremes_bit_exact(oracle_mod, b_col):
+    """K = 131071, the largest K whose int32 sums are exact: rows of all -128
+    against columns of all -128 reach 131071 * 16384 = 2147467264, just below
+    2^31; mixed with random rows.  Bit-exact against the oracle."""
+    M, N, K = 32, 48, 131071
+    A, B = operands("i8", b_col, M, N, K, 21)
+    A[:4, :K] = -128
+    if b_col:
+        B[:6, :K] = -128
+    else:
+        B[:K, :6] = -128
+    Cref = ref(oracle_mod, A, B, "i8", b_col, N, K)
+    assert Cref[0, 0] == 131071 * 16384
+    for v, s in [("auto", 0), ("direct", 3), ("sync", 1)]:
+        C = run(A, B, "i8", b_col, M, N, K, v, s)
+        assert np.array_equal(C, Cref)
+
+
+def test_fp16_very_long_k(oracle_mod):
+    """K = 2^20: 32768 K tiles through the ring (plus a 7-wide tail)."""
+    M, N, K = 16, 40, (1 << 20) + 7
+    A, B = operands("f16", False, M, N, K, 22)
+    C = run(A, B, "f16", False, M, N, K)
+    parity.check_full(C, ref(oracle_mod, A, B, "f16", False, N, K), A, B, "f16", False, M, N, K)
+
+
+def test_large_output_sampled(oracle_mod):
+    """C of 16384 x 16384 fp32 (1 GiB) from K = 64: every output written, sampled
+    entries against the oracle."""
+    sampled(oracle_mod, I.Workload("fp16 GEMM 16384x16384x64", 23, "f16", 16384, 16384, 64), n=2000)
