@@ -421,6 +421,11 @@ def main():
                               "pct_of_hbm": round(100 * wk.alg_bytes / (t * 1e-3) / 1e9 / HBM_GBS, 1),
                               "unpipelined_us": round(t1 * 1e3, 2),
                               "speedup_vs_unpipelined": round(t1 / t, 3)}
+            if wk is I.W_I8_4096 and not args.no_power:  # the int8 compute roof for this data
+                ceil = mfma_ceiling(p, 2.0)
+                if ceil:
+                    extra[wk.name]["mfma_ceiling_tops"] = ceil
+                    extra[wk.name]["value_over_ceiling"] = round(tf / ceil, 4)
             del p
         out["workloads"] = extra
 
