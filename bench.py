@@ -401,6 +401,12 @@ def main():
             by = {(d["tile"], d["variant"], d["stages"]): d["tflops"] for d in sweep}
             # speedup of each pipelined form over the unpipelined SYNC loop of the same tile:
             # the pages' 128 x 256 x 32 tile, and the tile of the headline
+            pg = by.get((1, "direct", 3))
+            if pg:  # the pages' shape: 128 x 256 x 32 fp16 tile, 256 threads, 3-stage ring
+                out["pages_shape"] = {"tile": "128x256x32", "threads": 256, "variant": "direct", "stages": 3,
+                                      "tflops": pg, "pct_of_peak": round(100 * pg / PEAK_TFLOPS["f16"], 1),
+                                      "speedup_vs_unpipelined": round(pg / by[(1, "sync", 1)], 3)
+                                      if (1, "sync", 1) in by else None}
             for name, t in (("pipelining_speedup_pages_tile", 1), ("pipelining_speedup_headline_tile", plan.tile_id)):
                 base = by.get((t, "sync", 1))
                 if base:
