@@ -75,17 +75,32 @@ enum spt_layout { SPT_ROW = 0, SPT_COL = 1 };
  *          on CDNA4 the buffer_load ... lds instruction, which bypasses the
  *          VGPRs), in an S-stage LDS ring with S = 2, 3 or 4 ("Hiding Memory
  *          Latency ...", sections 5 and 6).
+ *  PERSIST the DIRECT ring run by persistent workgroups, two per CU (at
+ *          most 512), each walking a stream of output tiles ("Hiding Memory
+ *          Latency ...", section 8, closing remark on independent tile
+ *          streams).  The ring runs on across tile boundaries, and each wave
+ *          keeps two accumulator sets, so that the C store of one tile is
+ *          issued during the K-loop of the next instead of after it (the
+ *          epilogue of section 5 taken off the critical path).  Only the
+ *          SPT_TILE_128x128 tile; only shapes with M % 128 == 0, N % 128 ==
+ *          0, K % BK == 0 and an even number K / BK >= 2 of K tiles (>= 4
+ *          for a 4-stage ring); SPT_ERR_UNSUPPORTED otherwise.  Never
+ *          chosen by AUTO: on MI355X it measures slower than DIRECT (a
+ *          wave's stores and copies share one in-order completion counter,
+ *          so the ring's waits also wait for the overlapped stores).
  *  AUTO    the library's choice for the shape.
- * Valid (variant, stages) pairs: SYNC x 1, REG x {1,2}, DIRECT x {2,3,4};
+ * Valid (variant, stages) pairs: SYNC x 1, REG x {1,2}, DIRECT x {2,3,4},
+ * PERSIST x {2,3,4};
  * a ring of S stages must fit in the 160 KiB of LDS (SPT_ERR_UNSUPPORTED
  * otherwise).  stages = 0 picks the variant's default (SYNC 1, REG 2,
- * DIRECT 2 for tiles with a 128-byte K depth, else 3).
+ * DIRECT 2 for tiles with a 128-byte K depth, else 3; PERSIST 3).
  */
 enum spt_variant {
     SPT_VARIANT_AUTO = 0,
     SPT_VARIANT_SYNC = 1,
     SPT_VARIANT_REG = 2,
-    SPT_VARIANT_DIRECT = 3
+    SPT_VARIANT_DIRECT = 3,
+    SPT_VARIANT_PERSIST = 4
 };
 
 /*
@@ -133,7 +148,7 @@ typedef struct spt_plan_info {
     int32_t wave_m, wave_n;         /* per-wave output tile */
     int32_t elt_bytes;              /* bytes per A/B element */
     int64_t tiles_m, tiles_n;       /* workgroup tiles along M and N */
-    int64_t grid;                   /* workgroups launched = tiles_m * tiles_n */
+    int64_t grid;                   /* workgroups launched: tiles_m * tiles_n (PERSIST: at most 512) */
     int64_t k_tiles;                /* ceil(K / BK) */
     int64_t k_full_tiles;           /* floor(K / BK) */
     int32_t k_tail;                 /* K mod BK: width of the zero-filled last tile (0 = none) */
@@ -149,6 +164,10 @@ typedef struct spt_plan_info {
     int32_t mfma_per_ktile_per_wave;
     double ratio_flop_per_byte;     /* 2*BM*BN*BK / ((BM*BK + BK*BN)*elt) */
     double ratio_mfma_per_load;     /* MFMA instructions per global load instruction, per wave */
+    int32_t store_window;           /* PERSIST: K tiles (2, 4 or 8) over which a wave writes the
+                                       previous output tile (16 / store_window stores per K tile);
+                                       else 0 */
+    int32_t tiles_per_wg;           /* output tiles per workgroup: ceil(tiles_m * tiles_n / grid) */
 } spt_plan_info;
 
 /* C = A*B with B row-major, the library's choice of tile and variant. */

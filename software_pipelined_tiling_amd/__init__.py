@@ -17,7 +17,7 @@ __all__ = [
     "spt_gemm", "spt_gemm_ex", "spt_plan", "spt_status_string", "spt_last_error", "spt_version",
     "spt_scale_by_two", "spt_probe_mfma", "gemm", "plan", "scale_by_two", "SptError", "PlanInfo", "lib_path",
     "F16", "BF16", "I8", "F32", "ROW", "COL", "VARIANT_AUTO", "VARIANT_SYNC", "VARIANT_REG",
-    "VARIANT_DIRECT", "TILE_AUTO", "TILE_128x256", "TILE_256x256", "TILE_128x128", "TILE_256x256_4W",
+    "VARIANT_DIRECT", "VARIANT_PERSIST", "TILE_AUTO", "TILE_128x256", "TILE_256x256", "TILE_128x128", "TILE_256x256_4W",
     "TILE_256x256_4W_K64B",
 ]
 
@@ -27,12 +27,13 @@ lib_path = os.path.join(HERE, "libspt.so")
 # enum spt_dtype / spt_layout / spt_variant / spt_tile / spt_status
 F16, BF16, I8, F32 = 0, 1, 2, 3
 ROW, COL = 0, 1
-VARIANT_AUTO, VARIANT_SYNC, VARIANT_REG, VARIANT_DIRECT = 0, 1, 2, 3
+VARIANT_AUTO, VARIANT_SYNC, VARIANT_REG, VARIANT_DIRECT, VARIANT_PERSIST = 0, 1, 2, 3, 4
 TILE_AUTO, TILE_128x256, TILE_256x256, TILE_128x128, TILE_256x256_4W, TILE_256x256_4W_K64B = 0, 1, 2, 3, 4, 5
 SPT_OK, SPT_ERR_INVALID, SPT_ERR_UNSUPPORTED, SPT_ERR_MISALIGNED, SPT_ERR_LAUNCH = 0, -1, -2, -3, -4
 
 DTYPE_CODES = {"f16": F16, "bf16": BF16, "i8": I8, "f32": F32}
-VARIANT_CODES = {"auto": VARIANT_AUTO, "sync": VARIANT_SYNC, "reg": VARIANT_REG, "direct": VARIANT_DIRECT}
+VARIANT_CODES = {"auto": VARIANT_AUTO, "sync": VARIANT_SYNC, "reg": VARIANT_REG, "direct": VARIANT_DIRECT,
+                 "persist": VARIANT_PERSIST}
 
 
 class PlanInfo(ctypes.Structure):
@@ -51,6 +52,7 @@ class PlanInfo(ctypes.Structure):
         ("wg_per_cu_lds", ctypes.c_int32), ("waves_per_simd_lds", ctypes.c_int32),
         ("steady_vmcnt", ctypes.c_int32), ("mfma_per_ktile_per_wave", ctypes.c_int32),
         ("ratio_flop_per_byte", ctypes.c_double), ("ratio_mfma_per_load", ctypes.c_double),
+        ("store_window", ctypes.c_int32), ("tiles_per_wg", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:

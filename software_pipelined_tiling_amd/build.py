@@ -20,7 +20,7 @@ ARCH = "gfx950"
 
 SOURCES = [f"spt_kernels_{dt}_{lay}.hip" for dt in ("f16", "bf16", "i8", "f32") for lay in ("row", "col")]
 SOURCES += ["spt_stream.hip", "spt_probe.hip", "spt_api.cpp"]
-HEADERS = ["spt_kernel.hpp", "spt_instances.hpp", "spt_registry.h", "spt_config.h"]
+HEADERS = ["spt_kernel.hpp", "spt_persist.hpp", "spt_instances.hpp", "spt_registry.h", "spt_config.h"]
 
 # Packed-fp32 VALU instructions are disabled for all device code (-packed-fp32-ops).
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -35,13 +35,14 @@ static const KernelTable& table_for(int dtype, int bcol)
     return t[dtype][bcol ? 1 : 0];
 }
 
-const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int stages, int exact)
+const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int stages, int exact, int window)
 {
     if (dtype < 0 || dtype > 3) return nullptr;
     const KernelTable& t = table_for(dtype, bcol);
     for (int i = 0; i < t.count; ++i) {
         const KernelEntry& e = t.entries[i];
-        if (e.bcol == bcol && e.tile == tile && e.variant == variant && e.stages == stages && e.exact == exact)
+        if (e.bcol == bcol && e.tile == tile && e.variant == variant && e.stages == stages && e.exact == exact &&
+            e.window == window)
             return &e;
     }
     return nullptr;
@@ -50,30 +51,41 @@ const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int s
 // The library's default when the caller passes AUTO (chosen from measured
 // sweeps on MI355X).  Tile: 256 x 256 with one wave per SIMD (the least LDS and
 // global traffic per MFMA) when the shape is an exact multiple of it, its grid
-// gives each of the 256 CUs a workgroup and K spans at least 512 bytes (short K
-// is bound by the C store, where two 128 x 256 workgroups per CU overlap
-// better); else the 128 x 256 tile if its grid fills the CUs; else 128 x 128
-// for the most workgroups.  Variant: the DIRECT ring, 2 stages for 128-byte K
-// tiles (two fill the LDS), else 3.
+// gives each of the 256 CUs a workgroup and K spans at least 2 KiB of each row
+// (shorter K is bound by the C store and the per-tile ramp, where two 128 x 256
+// workgroups per CU do better: bf16 8192 x 8192 x 256 in 70 us against 79, x 512
+// in 97 against 101; x 1024 in 150 against 145); else the 128 x 256 tile if its
+// grid fills the CUs; else 128 x 128 for the most workgroups.  Variant: the
+// DIRECT ring, 2 stages for 128-byte K tiles (two fill the LDS), else 3.
 static constexpr int64_t kCus = 256;
 static void resolve(int dtype, int64_t M, int64_t N, int64_t K, int& variant, int& stages, int& tile)
 {
+    if (variant == V_PERSIST && tile == 0) tile = 3;
     if (tile == 0) {
         const int elt = elt_bytes(dtype);
         const int64_t bk4 = kTiles[4].BKB / elt;
-        const bool fits4 = M % 256 == 0 && N % 256 == 0 && K % bk4 == 0 && K * elt >= 512;
+        const bool fits4 = M % 256 == 0 && N % 256 == 0 && K % bk4 == 0 && K * elt >= 2048;
         const int64_t n4 = (M / 256) * (N / 256);
         const int64_t n1 = ((M + 127) / 128) * ((N + 255) / 256);
         tile = (fits4 && n4 >= kCus) ? 4 : n1 >= kCus ? 1 : 3;
     }
     if (variant == V_AUTO) variant = V_DIRECT;
-    if (stages == 0) stages = variant == V_SYNC ? 1 : variant == V_REG ? 2 : (kTiles[tile].BKB >= 128 ? 2 : 3);
+    if (stages == 0)
+        stages = variant == V_SYNC ? 1 : variant == V_REG ? 2 : variant == V_PERSIST ? 3 : (kTiles[tile].BKB >= 128 ? 2 : 3);
 }
+
+// PERSIST: the store window (K tiles over which the previous output tile is
+// written; 16 / window stores per K tile) for k_full K tiles: the longest of
+// 2, 4, 8 that fits (the built instantiations).  Two or more stores per K tile
+// keep the two 64-byte halves of every 128-byte line of C in one K tile (one
+// store per K tile split the lines and raised the HBM write traffic by a
+// fifth, measured).
+static int store_window(int64_t k_full) { return k_full >= 8 ? 8 : k_full >= 4 ? 4 : 2; }
 
 static bool valid_pair(int variant, int stages)
 {
     return (variant == V_SYNC && stages == 1) || (variant == V_REG && (stages == 1 || stages == 2)) ||
-           (variant == V_DIRECT && stages >= 2 && stages <= 4);
+           ((variant == V_DIRECT || variant == V_PERSIST) && stages >= 2 && stages <= 4);
 }
 
 // Checks every argument except the pointers; fills `pi` on success.
@@ -83,7 +95,7 @@ static int make_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, i
     if (dtype < 0 || dtype > 3) return fail(SPT_ERR_INVALID, "dtype %d is not an spt_dtype", dtype);
     if (b_layout != SPT_ROW && b_layout != SPT_COL)
         return fail(SPT_ERR_INVALID, "b_layout %d is not an spt_layout", b_layout);
-    if (variant < 0 || variant > 3) return fail(SPT_ERR_INVALID, "variant %d is not an spt_variant", variant);
+    if (variant < 0 || variant > 4) return fail(SPT_ERR_INVALID, "variant %d is not an spt_variant", variant);
     if (stages < 0 || stages > 4) return fail(SPT_ERR_INVALID, "stages %d not in 0..4", stages);
     if (tile < 0 || tile >= kNumTiles) return fail(SPT_ERR_INVALID, "tile_id %d is not an spt_tile", tile);
     if (M < 0 || N < 0 || K < 0) return fail(SPT_ERR_INVALID, "negative size");
@@ -93,6 +105,8 @@ static int make_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, i
     resolve(dtype, M, N, K, variant, stages, tile);
     if (!valid_pair(variant, stages))
         return fail(SPT_ERR_UNSUPPORTED, "variant %d has no %d-stage form", variant, stages);
+    if (variant == V_PERSIST && tile != 3)
+        return fail(SPT_ERR_UNSUPPORTED, "the persistent variant runs the 128 x 128 tile only");
 
     const TileShape& T = kTiles[tile];
     const int elt = elt_bytes(dtype);
@@ -116,6 +130,17 @@ static int make_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, i
     p.grid = p.tiles_m * p.tiles_n;
     p.k_tiles = (K + p.BK - 1) / p.BK;
     p.k_full_tiles = K / p.BK;
+    if (variant == V_PERSIST) {
+        // as many workgroups as the CUs hold at once: two per CU (64 x 64 per
+        // wave, two accumulator sets in 128 registers, two waves per SIMD).
+        // The grid stays a multiple of the 8 XCDs, so that a workgroup's tile
+        // stream stays on one XCD.  The previous tile's C is written over the
+        // store window.
+        const int64_t resident = kCus * 2;
+        if (p.grid > resident) p.grid = resident;
+        p.store_window = store_window(p.k_full_tiles);
+    }
+    p.tiles_per_wg = p.grid > 0 ? (int32_t)((p.tiles_m * p.tiles_n + p.grid - 1) / p.grid) : 0;
     p.k_tail = (int32_t)(K - p.k_full_tiles * p.BK);
     // "Pipeline GPU Kernel", Schritt 1: smem_a = BM*BK*sizeof(T), smem_b = BK*BN*sizeof(T).
     p.a_stage_bytes = p.BM * p.BK * elt;
@@ -132,6 +157,9 @@ static int make_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, i
     p.wg_per_cu_lds = kLdsPerCu / p.lds_bytes;
     p.waves_per_simd_lds = p.wg_per_cu_lds * p.waves / kSimdsPerCu;
     p.steady_vmcnt = variant == V_DIRECT ? (stages - 2) * (p.a_copies_per_thread + p.b_copies_per_thread) : 0;
+    if (variant == V_PERSIST)  // the younger copies, and the stores issued after the awaited copies
+        p.steady_vmcnt = (stages - 2) * (p.a_copies_per_thread + p.b_copies_per_thread) +
+                         (stages - 1) * ((p.wave_m / 16) * (p.wave_n / 16) / p.store_window);
     // one 16x16 MFMA step covers 64 bytes of k per lane group; fp32 issues 4 MFMAs per step
     const int kstep = 4 * (16 / elt);
     p.mfma_per_ktile_per_wave = (p.wave_m / 16) * (p.wave_n / 16) * (p.BK / kstep) * (dtype == DT_F32 ? 4 : 1);
@@ -182,8 +210,20 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     // register slot of step 0 alternates); the exact-fit form has no odd last tile.
     const bool one_step = kTiles[pi.tile_id].BKB == 64;
     const bool fits = M % pi.BM == 0 && N % pi.BN == 0 && pi.k_tail == 0 && (!one_step || pi.k_full_tiles % 2 == 0);
-    const KernelEntry* e = fits ? find_kernel(dtype, bcol, pi.tile_id, pi.variant, pi.stages, 1) : nullptr;
-    if (!e) e = find_kernel(dtype, bcol, pi.tile_id, pi.variant, pi.stages, 0);
+    const KernelEntry* e = nullptr;
+    if (pi.variant == V_PERSIST) {
+        if (!fits || pi.k_full_tiles < 2 || pi.store_window < pi.stages - 1)
+            return fail(SPT_ERR_UNSUPPORTED,
+                        "the persistent variant needs M %% %d == 0, N %% %d == 0 and an even number (>= %d) of "
+                        "whole K tiles of %d",
+                        pi.BM, pi.BN, pi.stages == 4 ? 4 : 2, pi.BK);
+        // the C store of one output tile is a 32-bit buffer range of BM row pitches
+        if ((int64_t)pi.BM * ldc * 4 >= lim) return fail(SPT_ERR_UNSUPPORTED, "C row panel exceeds 2 GiB");
+        e = find_kernel(dtype, bcol, pi.tile_id, pi.variant, pi.stages, 1, pi.store_window);
+    } else {
+        e = fits ? find_kernel(dtype, bcol, pi.tile_id, pi.variant, pi.stages, 1) : nullptr;
+        if (!e) e = find_kernel(dtype, bcol, pi.tile_id, pi.variant, pi.stages, 0);
+    }
     if (!e) return fail(SPT_ERR_UNSUPPORTED, "no kernel built for dtype %d layout %d tile %d variant %d stages %d",
                         dtype, b_layout, pi.tile_id, pi.variant, pi.stages);
 

@@ -7,7 +7,7 @@
 namespace spt {
 
 enum DType { DT_F16 = 0, DT_BF16 = 1, DT_I8 = 2, DT_F32 = 3 };
-enum Variant { V_AUTO = 0, V_SYNC = 1, V_REG = 2, V_DIRECT = 3 };
+enum Variant { V_AUTO = 0, V_SYNC = 1, V_REG = 2, V_DIRECT = 3, V_PERSIST = 4 };
 
 // One workgroup tile: BM x BN outputs, K depth of BKB bytes per row (BK =
 // BKB / elt elements), WAVES_M x WAVES_N waves of 64 lanes.

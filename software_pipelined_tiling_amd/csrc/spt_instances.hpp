@@ -4,6 +4,7 @@
 #pragma once
 
 #include "spt_kernel.hpp"
+#include "spt_persist.hpp"
 #include "spt_registry.h"
 
 namespace spt {
@@ -19,9 +20,32 @@ template <int DT, int BC, int TI, int V, int S, int EX = 0>
 constexpr KernelEntry entry()
 {
     typedef Cfg<DT, BC != 0, TI, V, S, EX != 0> C;
-    return KernelEntry{DT, BC, TI, V, S, EX, C::THREADS, C::LDS_BYTES, C::LOADS, &launch_gemm<C>,
+    return KernelEntry{DT, BC, TI, V, S, EX, 0, C::THREADS, C::LDS_BYTES, C::LOADS, &launch_gemm<C>,
                        (const void*)&gemm_kernel<C>};
 }
+
+// Persistent workgroups (spt_persist.hpp): the 128 x 128 tile, exact fit, a
+// ring of S stages, the previous tile's C written over P K tiles.
+template <class C, int P>
+hipError_t launch_persist(const GemmArgs& a, unsigned grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((gemm_persist_kernel<C, P>), dim3(grid), dim3(C::THREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int DT, int BC, int TI, int S, int P>
+constexpr KernelEntry pentry()
+{
+    typedef Cfg<DT, BC != 0, TI, V_PERSIST, S, true> C;
+    return KernelEntry{DT, BC, TI, V_PERSIST, S, 1, P, C::THREADS, C::LDS_BYTES, C::LOADS, &launch_persist<C, P>,
+                       (const void*)&gemm_persist_kernel<C, P>};
+}
+// Windows of 2, 4 and 8 K tiles (8, 4 or 2 stores per K tile of the 16
+// blocks of a 64 x 64 wave tile); a window covers at least S-1 K tiles.
+#define SPT_PERSIST(DT, BC)                                                                          \
+    pentry<DT, BC, 3, 2, 2>(), pentry<DT, BC, 3, 2, 4>(), pentry<DT, BC, 3, 2, 8>(),                 \
+        pentry<DT, BC, 3, 3, 2>(), pentry<DT, BC, 3, 3, 4>(), pentry<DT, BC, 3, 3, 8>(),             \
+        pentry<DT, BC, 3, 4, 4>(), pentry<DT, BC, 3, 4, 8>()
 
 // Every (variant, stages) pair of the boundary for one (dtype, layout, tile).
 #define SPT_PAIRS(DT, BC, TI)                                                              \
@@ -43,7 +67,7 @@ constexpr KernelEntry entry()
 #define SPT_DEFINE_TABLE(NAME, DT, BC)                                                          \
     static const KernelEntry k_##NAME[] = {                                                    \
         SPT_TILE_ALL(DT, BC, 1), SPT_TILE_BIG(DT, BC, 2), SPT_PAIRS(DT, BC, 3), SPT_RING34(DT, BC, 3), \
-        SPT_TILE_BIG(DT, BC, 4), SPT_TILE_ALL(DT, BC, 5),                                      \
+        SPT_TILE_BIG(DT, BC, 4), SPT_TILE_ALL(DT, BC, 5), SPT_PERSIST(DT, BC),                 \
     };                                                                                         \
     KernelTable kernels_##NAME() { return KernelTable{k_##NAME, (int)(sizeof(k_##NAME) / sizeof(k_##NAME[0]))}; }
 

@@ -139,7 +139,9 @@ struct Cfg {
     // 16x16 wave tiles of 128 x 128 need the whole register file: one wave per
     // SIMD; so does a ring that leaves LDS for one workgroup of four waves per CU
     static constexpr int WG_PER_CU_LDS = kLdsPerCu / LDS_BYTES;
-    static constexpr int WAVES_PER_SIMD = (FM * FN > 32 || WG_PER_CU_LDS * WAVES < 8) ? 1 : 2;
+    // (V_PERSIST keeps two accumulator sets per wave: twice the accumulators)
+    static constexpr int WAVES_PER_SIMD =
+        ((V_ == V_PERSIST ? 2 : 1) * FM * FN > 32 || WG_PER_CU_LDS * WAVES < 8) ? 1 : 2;
 
     static_assert(BK % KSTEP == 0, "BK must hold whole MFMA steps");
     static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0,
@@ -149,6 +151,7 @@ struct Cfg {
     static_assert(V_ != V_SYNC || S_ == 1, "SYNC has one stage");
     static_assert(V_ != V_REG || (S_ == 1 || S_ == 2), "REG has 1 or 2 stages");
     static_assert(V_ != V_DIRECT || (S_ >= 2 && S_ <= 4), "DIRECT has 2 to 4 stages");
+    static_assert(V_ != V_PERSIST || (S_ >= 2 && S_ <= 4 && EXACT_), "PERSIST: exact-fit 2- to 4-stage rings");
     static_assert((S_ - 1) * LOADS < 64, "vmcnt range");
 };
 
@@ -398,7 +401,7 @@ struct Gemm {
     static constexpr int DMA_BIAS = 3072;
     static __device__ __forceinline__ constexpr int dma_bias(int i)
     {
-        return C::V == V_DIRECT ? DMA_BIAS - (i % 4) * 1024 : 0;
+        return (C::V == V_DIRECT || C::V == V_PERSIST) ? DMA_BIAS - (i % 4) * 1024 : 0;
     }
     struct Copy {
         int a_voff[C::A_CPT];

@@ -12,6 +12,7 @@ typedef hipError_t (*LaunchFn)(const GemmArgs&, unsigned grid, hipStream_t);
 
 struct KernelEntry {
     int dtype, bcol, tile, variant, stages, exact;
+    int window;  // V_PERSIST: K tiles over which a wave writes the previous output tile (else 0)
     int threads, lds_bytes, loads_per_tile;
     LaunchFn launch;
     const void* kernel;
@@ -41,6 +42,6 @@ hipError_t launch_mfma_probe(int dtype, const void* ops, int64_t n_vec, int64_t 
 
 // nullptr when that combination is not built.  exact = 1 asks for the
 // instantiation that assumes M, N, K are multiples of the tile.
-const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int stages, int exact);
+const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int stages, int exact, int window = 0);
 
 }  // namespace spt

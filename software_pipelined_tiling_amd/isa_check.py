@@ -172,6 +172,90 @@ def load(lib: Optional[str] = None) -> List[Kernel]:
 
 
 @dataclasses.dataclass
+class PersistKernel(Kernel):
+    window: int = 0  # K tiles over which the previous output tile is stored
+
+
+_PERSIST = re.compile(r"gemm_persist_kernelI.*?EELi(\d+)EE")
+
+
+def load_persist(lib: Optional[str] = None) -> List[PersistKernel]:
+    """The persistent-workgroup kernels (csrc/spt_persist.hpp)."""
+    lib = lib or os.path.join(HERE, "libspt.so")
+    ks: List[PersistKernel] = []
+    for co in code_objects(lib):
+        meta = _metadata(co)
+        for name, instrs in _disassemble(co).items():
+            m, w = _CFG.search(name), _PERSIST.search(name)
+            if not (m and w):
+                continue
+            dt, bc, ti, _v, s, ex, _bl = (int(x) for x in m.groups())
+            ks.append(PersistKernel(name, dt, bool(bc), ti, "persist", s, bool(ex), instrs,
+                                    meta.get(name, {}), int(w.group(1))))
+    return ks
+
+
+def persist_stats(k: PersistKernel) -> dict:
+    """Figures of the steady loop of a persistent kernel: the shortest loop body
+    holding the MFMAs of two K tiles (the loop past the store window), plus
+    every vmcnt wait of the whole kernel."""
+    g = k.geometry
+    bodies = [b for b in loop_regions(k) if _count_mfma(b) == 2 * g["mfma_per_tile"]]
+    body = min(bodies, key=len) if bodies else []
+    vm_all = [int(m.group(1)) for x in k.instrs for m in [re.search(r"vmcnt\((\d+)\)", _op(x))] if m]
+    # copies before stores within every K tile: split the body (read as a cycle) at its barriers
+    order_ok = bool(body)
+    if body and any(x.startswith("s_barrier") for x in body):
+        b0 = next(i for i, x in enumerate(body) if x.startswith("s_barrier"))
+        rot = body[b0:] + body[:b0]
+        seg: List[str] = []
+        segs: List[List[str]] = []
+        for x in rot:
+            if x.startswith("s_barrier") and seg:
+                segs.append(seg)
+                seg = []
+            seg.append(x)
+        segs.append(seg)
+        for sg in segs:
+            cp = [i for i, x in enumerate(sg) if x.startswith("buffer_load") and x.rstrip().endswith("lds")]
+            st = [i for i, x in enumerate(sg) if x.startswith("buffer_store")]
+            if cp and st and max(cp) > min(st):
+                order_ok = False
+    return dict(
+        instructions=len(body), mfma=_count_mfma(body), dma=_count_copies(body),
+        stores=sum(x.startswith("buffer_store") for x in body),
+        barriers=sum(x.startswith("s_barrier") for x in body),
+        vmcnt_waits=[int(m.group(1)) for x in body for m in [re.search(r"vmcnt\((\d+)\)", x)] if m],
+        kernel_vmcnt_waits=sorted(set(vm_all)),
+        scratch=sum(x.startswith("scratch_") for x in body),
+        acc_moves=sum(x.startswith("v_accvgpr") for x in body),
+        copies_before_stores=order_ok,
+    )
+
+
+def check_persist(k: PersistKernel) -> Dict[str, bool]:
+    """The persistent kernel's schedule: per K tile of its steady loop the MFMAs,
+    copies and one barrier of the ring plus (wave-tile blocks) / window stores, issued after the
+    copies; one steady vmcnt wait, (S-2) x copies + (S-1) x stores per K tile;
+    the kernel's other waits only the prologue's and the final drain; no spills
+    or accumulator copies in the loop; the LDS ring of S stages."""
+    g, st = k.geometry, persist_stats(k)
+    BM, BN, _bkb, WM, WN = TILES[k.tile]
+    S, L, ST = k.stages, g["loads_per_tile"], (BM // WM // 16) * (BN // WN // 16) // k.window
+    steady = (S - 2) * L + (S - 1) * ST
+    first = (S - 1) * L + S * ST
+    return {
+        "counts": (st["mfma"] == 2 * g["mfma_per_tile"] and st["dma"] == 2 * L and st["stores"] == 2 * ST
+                   and st["barriers"] == 2),
+        "vmcnt": bool(st["vmcnt_waits"]) and all(v == steady for v in st["vmcnt_waits"]),
+        "kernel_vmcnt": set(st["kernel_vmcnt_waits"]) <= {steady, first, 0},
+        "order": st["copies_before_stores"],
+        "clean": st["scratch"] == 0 and st["acc_moves"] == 0,
+        "lds": k.meta.get("lds") == S * g["stage_bytes"],
+    }
+
+
+@dataclasses.dataclass
 class StreamKernel:
     name: str
     stages: int

@@ -135,6 +135,41 @@ def test_pages_tile_plan(L):
     assert pi.grid == 512 and pi.k_tiles == 128
 
 
+# ---- the persistent variant ---------------------------------------------------
+@pytest.mark.parametrize("K,window", [(64, 2), (128, 4), (192, 4), (256, 8), (512, 8), (4096, 8)])
+def test_persist_plan(L, K, window):
+    """bf16 8192 x 8192: 4096 tiles of 128 x 128 over 512 persistent workgroups
+    (two per CU), eight each; the store window is the longest of 2, 4, 8 K tiles
+    that fits; the steady wait leaves the younger copies and the stores
+    issued after the awaited copies in flight."""
+    rc, pi = spt.spt_plan(spt.BF16, 8192, 8192, K, spt.ROW, spt.VARIANT_PERSIST, 0, 0)
+    assert rc == 0, spt.spt_last_error()
+    assert (pi.tile_id, pi.stages, pi.BM, pi.BN, pi.BK) == (3, 3, 128, 128, 32)
+    assert pi.grid == 512 and pi.tiles_per_wg == 8 and pi.store_window == window
+    assert pi.lds_bytes == 3 * 16384
+    assert pi.steady_vmcnt == 1 * 4 + 2 * (16 // window)
+
+
+def test_persist_plan_small_grid_and_errors(L):
+    rc, pi = spt.spt_plan(spt.F16, 384, 512, 64, spt.ROW, spt.VARIANT_PERSIST, 2, 3)
+    assert rc == 0 and pi.grid == 12 and pi.tiles_per_wg == 1
+    rc, pi = spt.spt_plan(spt.F16, 4096, 4096, 64, spt.ROW, spt.VARIANT_DIRECT, 3, 1)
+    assert rc == 0 and pi.store_window == 0 and pi.tiles_per_wg == 1
+    assert spt.spt_plan(spt.F16, 512, 512, 64, spt.ROW, spt.VARIANT_PERSIST, 3, 1)[0] == -2
+    assert spt.spt_plan(spt.F16, 512, 512, 64, spt.ROW, spt.VARIANT_PERSIST, 1, 0)[0] == -2
+
+
+@pytest.mark.parametrize("M,N,K,st,tile", [
+    (100, 256, 64, 3, 0), (128, 200, 64, 3, 0), (128, 256, 70, 3, 0), (128, 256, 96, 3, 0),
+    (128, 256, 32, 3, 0), (128, 256, 64, 4, 0), (128, 256, 64, 3, 1), (128, 256, 0, 3, 0)])
+def test_persist_rejects_unfit_shapes(L, M, N, K, st, tile):
+    """Outside its scope (a ragged M or N, a K tail, an odd count of K tiles, one
+    K tile, a 4-stage ring over 2 K tiles, another tile, K = 0) the persistent
+    variant returns SPT_ERR_UNSUPPORTED before any HIP call."""
+    assert ex(M=M, N=N, K=K, lda=max(8, -(-K // 8) * 8), var=spt.VARIANT_PERSIST, st=st, tile=tile) == -2
+    assert spt.spt_last_error() != ""
+
+
 # ---- the streaming pipeline y = 2x: validation before any HIP call -----------
 X0, Y0 = 0x100000, 0x200000   # fake, aligned, far apart
 

@@ -119,3 +119,17 @@ def test_streaming_ring_schedule(built_lib):
     for k in ks:
         res = X.check_stream(k)
         assert all(res.values()), (k.name, res)
+
+
+def test_persistent_ring_schedule(built_lib):
+    """The persistent kernels (128 x 128 tile, windows of 2, 4 and 8 K tiles): per
+    K tile of the steady loop the MFMAs, copies and barrier of the ring plus
+    16 / window stores, issued after the K tile's copies; one steady vmcnt wait
+    of (S-2) x copies + (S-1) x stores, the kernel's other waits only the
+    prologue's and the final drain; no spills or accumulator copies in the loop."""
+    ks = X.load_persist()
+    assert len(ks) == 8 * 8
+    assert {(k.stages, k.window) for k in ks} == {(2, 2), (2, 4), (2, 8), (3, 2), (3, 4), (3, 8), (4, 4), (4, 8)}
+    for k in ks:
+        res = X.check_persist(k)
+        assert all(res.values()), (k.name, res, X.persist_stats(k))
