@@ -89,6 +89,33 @@ class Problem:
                 spt.COL if w.b_col else spt.ROW, spt.VARIANT_CODES[variant], stages, tile)
 
 
+def c_store_only(prob: Problem, steps: int):
+    """Microseconds per call of the plan the library picks for `prob`, run with K = 0:
+    the kernel then only writes C (zeros), the floor under the C store of that plan."""
+    import torch
+    import software_pipelined_tiling_amd as spt
+    w = prob.w
+    rc, pi = spt.spt_plan(spt.DTYPE_CODES[w.dtype], w.M, w.N, w.K, spt.COL if w.b_col else spt.ROW)
+    if rc != 0:
+        return None
+    stream = torch.cuda.current_stream()
+    a = (w.M, w.N, 0, prob.dA.data_ptr(), prob.A.shape[1], prob.dB.data_ptr(), prob.B.shape[1],
+         prob.C.data_ptr(), w.N, spt.DTYPE_CODES[w.dtype], stream.cuda_stream, spt.COL if w.b_col else spt.ROW,
+         pi.variant, pi.stages, pi.tile_id)
+    if spt.spt_gemm_ex(*a) != 0:
+        return None
+    for _ in range(20):
+        spt.spt_gemm_ex(*a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        spt.spt_gemm_ex(*a)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return round(e0.elapsed_time(e1) / steps * 1e3, 2)
+
+
 def time_calls(prob: Problem, steps: int, warmup: int, variant="auto", stages=0, tile=0):
     """Mean ms per call over `steps` back-to-back calls, HIP events on the launch stream."""
     import torch
@@ -427,6 +454,9 @@ def main():
                               "pct_of_hbm": round(100 * wk.alg_bytes / (t * 1e-3) / 1e9 / HBM_GBS, 1),
                               "unpipelined_us": round(t1 * 1e3, 2),
                               "speedup_vs_unpipelined": round(t1 / t, 3)}
+            if wk.K <= 1024 and wk.M * wk.N >= 1 << 24:
+                # the C store alone: the same kernel with K = 0 (it writes zeros to all of C)
+                extra[wk.name]["c_store_only_us"] = c_store_only(p, steps)
             if wk is I.W_I8_4096 and not args.no_power:  # the int8 compute roof for this data
                 ceil = mfma_ceiling(p, 2.0)
                 if ceil:

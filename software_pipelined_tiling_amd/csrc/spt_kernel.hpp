@@ -475,8 +475,12 @@ struct Gemm {
     };
     static __device__ __forceinline__ i32x4_t desc(uint64_t base, uint32_t bytes)
     {
-        // base < 2^47 (checked on the host): word 1 holds its high bits with stride 0
-        return (i32x4_t){(int)(uint32_t)base, (int)(uint32_t)(base >> 32), (int)bytes, 0x00020000};
+        // base < 2^47 (checked on the host): word 1 holds its high bits with stride 0.
+        // The words are wave-uniform; readfirstlane keeps them in scalar registers even
+        // where they come from vector-ALU arithmetic (the copies take them only there).
+        return (i32x4_t){__builtin_amdgcn_readfirstlane((int)(uint32_t)base),
+                         __builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32)),
+                         __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
     }
     static __device__ __forceinline__ void ring_init(const GemmArgs& p, int m0, int n0, int wave,
                                                      const SPT_LDS char* smem, Ring& r)
@@ -883,7 +887,8 @@ struct Gemm {
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         int tm, tn;
         tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
-        const int m0 = tm * C::BM, n0 = tn * C::BN;
+        // (the divisions of the tile order may run on the vector ALU: keep the results scalar)
+        const int m0 = __builtin_amdgcn_readfirstlane(tm) * C::BM, n0 = __builtin_amdgcn_readfirstlane(tn) * C::BN;
         const int wm0 = (wave / C::WAVES_N) * C::WTM, wn0 = (wave % C::WAVES_N) * C::WTN;
         const int mb0 = wm0 / 16, nb0 = wn0 / 16;
 
