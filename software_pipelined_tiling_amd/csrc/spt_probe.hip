@@ -39,7 +39,14 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(const i32x4_t* ops, int
     }
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 64; ++i) s += (float)acc[i][0] + (float)acc[i][3];
+    for (int i = 0; i < 64; ++i) {
+        if constexpr (DT == DT_I8) {  // int32 sums held bit for bit in the float vector
+            const i32x4_t v = __builtin_bit_cast(i32x4_t, acc[i]);
+            s += (float)v[0] + (float)v[3];
+        } else {
+            s += acc[i][0] + acc[i][3];
+        }
+    }
     sink[g] = s;
 }
 
