@@ -24,6 +24,8 @@ Besides the headline value it reports, in the same line:
                 dense peak at that clock (context for the roofline fraction)
   mfma_ceiling  the rate MFMAs alone sustain with the headline's operand data
                 under the power limit (spt_probe_mfma), and value / that rate
+  vendor_hipblaslt  the vendor library (torch.mm with fp32 output, torch._int_mm
+                for int8) on the same operands, per workload too (context only)
 """
 from __future__ import annotations
 
@@ -87,6 +89,37 @@ class Problem:
         return (w.M, w.N, w.K, self.dA.data_ptr(), self.A.shape[1], self.dB.data_ptr(),
                 self.B.shape[1], self.C.data_ptr(), w.N, spt.DTYPE_CODES[w.dtype], stream,
                 spt.COL if w.b_col else spt.ROW, spt.VARIANT_CODES[variant], stages, tile)
+
+
+def vendor_us(prob: Problem, steps: int):
+    """Microseconds per call of the vendor library (hipBLASLt through torch) on the same
+    device operands and the same output type: torch.mm(..., out_dtype=float32) for
+    fp16/bf16, torch._int_mm for int8.  Context only; None where torch has no such call."""
+    import torch
+    w = prob.w
+    a = prob.dA[:, :w.K]
+    b = prob.dB[:, :w.K].t() if w.b_col else prob.dB[:w.K, :w.N]
+    if w.dtype == "i8":
+        fn = lambda: torch._int_mm(a, b)
+    elif w.dtype in ("f16", "bf16"):
+        fn = lambda: torch.mm(a, b, out_dtype=torch.float32)
+    else:
+        return None
+    try:
+        fn()
+        for _ in range(20):
+            fn()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return round(e0.elapsed_time(e1) / steps * 1e3, 2)
+    except Exception:  # shape or type torch does not support
+        return None
 
 
 def c_store_only(prob: Problem, steps: int):
@@ -383,7 +416,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name + ", A/B row-major, fp32 accumulate, fp32 C, U[-1,1] fp16",
                    "tile": f"{plan.BM}x{plan.BN}x{plan.BK}", "threads": plan.threads,
-                   "variant": {1: "sync", 2: "reg", 3: "direct"}[plan.variant],
+                   "variant": {1: "sync", 2: "reg", 3: "direct", 4: "persist"}[plan.variant],
                    "stages": plan.stages, "pct_of_peak": round(100 * tflops / PEAK_TFLOPS["f16"], 1)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_TFLOPS["f16"],
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS["f16"], 4),
@@ -410,6 +443,13 @@ def main():
                                    "what": "spt_probe_mfma: 16x16x32 fp16 MFMAs alone, operands = the headline's "
                                            "A matrix (and, for comparison, zeros), one wave per SIMD on every CU, "
                                            "sustained 2 s each"}
+
+    if not args.only_headline:
+        vu = vendor_us(head, 50)
+        if vu:
+            out["vendor_hipblaslt"] = {"us": vu, "tflops": round(w.flops / (vu * 1e-6) / 1e12, 1),
+                                       "value_over_vendor": round(vu / (ms * 1e3), 3),
+                                       "what": "torch.mm(A, B, out_dtype=float32) on the same operands (context)"}
 
     if args.only_workload:
         args.no_sweep = True
@@ -454,6 +494,7 @@ def main():
                               "pct_of_hbm": round(100 * wk.alg_bytes / (t * 1e-3) / 1e9 / HBM_GBS, 1),
                               "unpipelined_us": round(t1 * 1e3, 2),
                               "speedup_vs_unpipelined": round(t1 / t, 3)}
+            extra[wk.name]["vendor_hipblaslt_us"] = vendor_us(p, steps)
             if wk.K <= 1024 and wk.M * wk.N >= 1 << 24:
                 # the C store alone: the same kernel with K = 0 (it writes zeros to all of C)
                 extra[wk.name]["c_store_only_us"] = c_store_only(p, steps)
