@@ -176,15 +176,25 @@ def gemm(A, B, out=None, *, b_layout: str = "row", variant: str = "auto", stages
     d = _torch_dtype_code(A)
     if A.dim() != 2 or B.dim() != 2 or A.stride(1) != 1 or B.stride(1) != 1:
         raise ValueError("A and B must be 2-D with unit column stride")
+    if not A.is_cuda or B.device != A.device:
+        raise ValueError("A and B must be on the same GPU")
+    if b_layout not in ("row", "col"):
+        raise ValueError("b_layout must be 'row' or 'col'")
     col = b_layout == "col"
     M = A.shape[0]
     K = A.shape[1] if K is None else K
     if N is None:
         N = B.shape[0] if col else B.shape[1]
+    # the kernels read K columns of A and K x N of B: both must lie inside the tensors
+    b_k, b_n = (B.shape[1], B.shape[0]) if col else (B.shape[0], B.shape[1])
+    if not (0 <= K <= A.shape[1] and K <= b_k and 0 <= N <= b_n):
+        raise ValueError(f"K={K}, N={N} exceed the operands A {tuple(A.shape)}, B {tuple(B.shape)}")
+    c_dtype = torch.int32 if d == I8 else torch.float32
     if out is None:  # row pitch padded to 16 bytes; the result is the (M, N) view
         ldc = -(-max(N, 1) // 4) * 4
-        out = torch.empty((M, ldc), dtype=torch.int32 if d == I8 else torch.float32,
-                          device=A.device)[:, :N]
+        out = torch.empty((M, ldc), dtype=c_dtype, device=A.device)[:, :N]
+    if out.dtype != c_dtype or out.device != A.device:
+        raise TypeError(f"out must be {c_dtype} on {A.device}")
     if out.dim() != 2 or out.stride(1) != 1 or out.shape[0] != M or out.shape[1] < N:
         raise ValueError("out must be (M, >=N) with unit column stride")
     if stream is None:
@@ -203,10 +213,14 @@ def scale_by_two(x, out=None, *, stages: int = 0, blocks: int = 0, stream=None):
     import torch
     if x.dtype != torch.float32 or not x.is_contiguous():
         raise TypeError("x must be a contiguous float32 tensor")
+    if not x.is_cuda:
+        raise ValueError("x must be on the GPU")
     if out is None:
         out = torch.empty_like(x)
     if out.dtype != torch.float32 or not out.is_contiguous() or out.numel() != x.numel():
         raise ValueError("out must be a contiguous float32 tensor of x's size")
+    if out.device != x.device:
+        raise ValueError("out must be on x's GPU")
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
     rc = spt_scale_by_two(x.numel(), x.data_ptr(), out.data_ptr(), stages, blocks, stream)

@@ -223,6 +223,30 @@ def test_torch_wrapper(oracle_mod):
     parity.check_full(out.cpu().numpy(), Cref, A, B, "f16", True, M, N, K)
 
 
+def test_torch_wrapper_rejects_unsafe_arguments():
+    """The wrapper refuses, before any launch, what would make a kernel read or
+    write outside the tensors: an output of the wrong dtype or device, K or N
+    beyond the operands, operands on different devices."""
+    A = torch.zeros((64, 64), dtype=torch.float16, device="cuda")
+    B = torch.zeros((64, 64), dtype=torch.float16, device="cuda")
+    with pytest.raises(TypeError):
+        spt.gemm(A, B, out=torch.zeros((64, 64), dtype=torch.float16, device="cuda"))
+    with pytest.raises(TypeError):
+        spt.gemm(A, B, out=torch.zeros((64, 64), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        spt.gemm(A, B, K=80)
+    with pytest.raises(ValueError):
+        spt.gemm(A, B, N=72)
+    with pytest.raises(ValueError):
+        spt.gemm(A, B, b_layout="col", N=65)
+    with pytest.raises(ValueError):
+        spt.gemm(A, B.cpu())
+    with pytest.raises(ValueError):
+        spt.gemm(A, B, b_layout="columns")
+    C = spt.gemm(A, B, K=48, N=40)  # within the operands: fine
+    assert tuple(C.shape) == (64, 40)
+
+
 # ---------------------------------------------------------------------------
 # Full-size workloads, in the launch configurations the benchmark times;
 # sampled outputs are recomputed one by one by the oracle.

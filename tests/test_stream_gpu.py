@@ -106,3 +106,11 @@ def test_torch_wrapper(oracle_mod):
     y = spt.scale_by_two(torch.from_numpy(x).cuda())
     torch.cuda.synchronize()
     same(y.cpu().numpy(), oracle_mod.scale_by_two(x))
+
+
+def test_torch_wrapper_rejects_host_tensors():
+    """A host tensor never reaches the kernel (its pointer is not a device address)."""
+    with pytest.raises(ValueError):
+        spt.scale_by_two(torch.ones(1024))
+    with pytest.raises(ValueError):
+        spt.scale_by_two(torch.ones(1024, device="cuda"), out=torch.empty(1024))
