@@ -33,6 +33,10 @@
  * K*ldb (row-major) or N*ldb (column-major) elements; padding beyond K or N
  * never enters the result.
  *
+ * Aliasing.  C must not share a byte with the used part of A (from A to the
+ * end of row M-1's first K elements) or of B (to the end of the last used
+ * row or column); such calls return SPT_ERR_INVALID.  A and B may overlap.
+ *
  * Ownership.  All matrix pointers are DEVICE pointers owned by the caller.
  * The library never allocates or frees device memory and keeps no pointer
  * after a call returns.  `stream` is a hipStream_t (NULL = the null
@@ -129,8 +133,10 @@ enum spt_tile {
 
 enum spt_status {
     SPT_OK = 0,
-    SPT_ERR_INVALID = -1,     /* negative size, null pointer, pitch too small, bad enum */
+    SPT_ERR_INVALID = -1,     /* negative size, null pointer, pitch too small, bad enum, C overlapping
+                                 A or B */
     SPT_ERR_UNSUPPORTED = -2, /* (variant, stages, tile, dtype, layout) not built; int8 K > 131071;
+                                 more than 2^31 - 4097 output tiles;
                                  an operand panel too large for 32-bit buffer offsets; A or B
                                  below 64 KiB or at or above 2^47 (the 48-bit base of a buffer
                                  descriptor) */

@@ -202,7 +202,19 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     const int64_t lim = INT64_C(0x7ffffff0);
     if ((int64_t)pi.BM * lda * elt >= lim || (bcol ? (int64_t)pi.BN * ldb * elt : (int64_t)pi.BK * ldb * elt) >= lim)
         return fail(SPT_ERR_UNSUPPORTED, "operand panel exceeds 2 GiB of buffer offsets");
-    if (pi.grid > INT32_MAX) return fail(SPT_ERR_UNSUPPORTED, "too many workgroups");
+    // (tile indices, and a persistent stream's next index, are 32-bit in the kernels)
+    if (pi.grid > INT32_MAX || pi.tiles_m * pi.tiles_n > INT32_MAX - 4096)
+        return fail(SPT_ERR_UNSUPPORTED, "too many output tiles");
+    // C is written while A and B are read: it must not share a byte with either
+    // (the byte ranges from each base to the end of its last row's used part)
+    if (K > 0) {
+        const uintptr_t c0 = (uintptr_t)C, c1 = c0 + (uintptr_t)((M - 1) * ldc + N) * 4;
+        const uintptr_t a0 = (uintptr_t)A, a1 = a0 + (uintptr_t)((M - 1) * lda + K) * elt;
+        const uintptr_t b0 = (uintptr_t)B,
+                        b1 = b0 + (uintptr_t)(bcol ? (N - 1) * ldb + K : (K - 1) * ldb + N) * elt;
+        if ((c0 < a1 && a0 < c1) || (c0 < b1 && b0 < c1))
+            return fail(SPT_ERR_INVALID, "C overlaps A or B");
+    }
 
     // The exact-fit instantiation when M, N and K are multiples of the tile
     // (same arithmetic, no tail or edge code), else the general one.

@@ -74,6 +74,19 @@ def test_validation_errors(L, kw, status):
     assert spt.spt_last_error() != ""
 
 
+@pytest.mark.parametrize("kw", [dict(C=PA), dict(C=PA + 0x1000), dict(C=PB), dict(C=PB + 0x1FF0),
+                                dict(C=PA - 0x3FF0), dict(lay=spt.COL, C=PB + 0x10)])
+def test_output_overlapping_an_operand_is_refused(L, kw):
+    """C written while A and B are read: any shared byte is refused before a launch
+    (a C starting 16 bytes less than its size below A ends inside A's first row)."""
+    assert ex(**kw) == -1
+    assert "overlap" in spt.spt_last_error()
+
+
+def test_too_many_output_tiles_is_refused(L):
+    assert ex(M=1 << 30, N=(1 << 31) - 16, ldc=(1 << 31) - 16) == -2
+
+
 def test_empty_problem_is_ok_without_launch(L):
     assert ex(M=0) == 0
     assert ex(N=0, ldb=1, ldc=1) == 0
