@@ -376,7 +376,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU; --gpus must be 1 "
+        print("bench.py: this benchmark runs on exactly one GPU; --gpus must be 1 "
               "(the GEMM shards over output tiles, see the sharding design notes).", file=sys.stderr)
         sys.exit(2)
 
