@@ -361,7 +361,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=300,
                     help="untimed calls first; the GPU's clock settles within ~30 ms of load")
     ap.add_argument("--tile", type=int, default=0, help="headline tile (0 = library default)")
-    ap.add_argument("--variant", default="auto", help="headline variant (auto/sync/reg/direct)")
+    ap.add_argument("--variant", default="auto", help="headline variant (auto/sync/reg/direct/persist)")
     ap.add_argument("--stages", type=int, default=0, help="headline stages (0 = variant default)")
     ap.add_argument("--cpu-budget", type=float, default=25.0, help="seconds of oracle CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
