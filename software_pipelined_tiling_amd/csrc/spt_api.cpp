@@ -49,14 +49,24 @@ const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int s
 }
 
 // The library's default when the caller passes AUTO (chosen from measured
-// sweeps on MI355X).  Tile: 256 x 256 with one wave per SIMD (the least LDS and
-// global traffic per MFMA) when the shape is an exact multiple of it, its grid
-// gives each of the 256 CUs a workgroup and K spans at least 2 KiB of each row
-// (shorter K is bound by the C store and the per-tile ramp, where two 128 x 256
-// workgroups per CU do better: bf16 8192 x 8192 x 256 in 70 us against 79, x 512
-// in 97 against 101; x 1024 in 150 against 145); else the 128 x 256 tile if its
-// grid fills the CUs; else 128 x 128 for the most workgroups.  Variant: the
-// DIRECT ring, 2 stages for 128-byte K tiles (two fill the LDS), else 3.
+// sweeps on MI355X).  Tile:
+//  - 256 x 256 with one wave per SIMD (the least LDS and global traffic per
+//    MFMA) when the shape is an exact multiple of it, its grid gives each of
+//    the 256 CUs a workgroup and K spans at least 2 KiB of each row (shorter K
+//    is bound by the C store, where two 128 x 256 workgroups per CU do better);
+//  - else 128 x 128 when the 128 x 256 grid leaves CUs without a workgroup;
+//  - else the 128 x 256 tile (two workgroups per CU) or the 256 x 256 tile of 8
+//    waves (one per CU), whichever leaves the lower load on the busiest CU,
+//    counted in 256 x 256 tiles with the larger tile's ~10% better throughput
+//    per FLOP.  The larger tile is taken only with K of at least 1 KiB per row,
+//    and, below 2 KiB, only when its grid fits in one round (a single resident
+//    workgroup per CU waits out each round's C store).  Measured fp16/bf16/int8:
+//    4000 x 3000 x 1000..4000, 3000^3, 5000^2 x 1024 and 8000 x 2000 x 8000
+//    run 4-25% faster on the 256 x 256 tile; 2000 x 4000 x 1000, 4100^3 and
+//    6000^2 x 2000, whose large tiles leave CUs idle or a long partial round,
+//    run faster on 128 x 256.
+// Variant: the DIRECT ring, 2 stages for 128-byte K tiles (two fill the LDS),
+// else 3.
 static constexpr int64_t kCus = 256;
 static void resolve(int dtype, int64_t M, int64_t N, int64_t K, int& variant, int& stages, int& tile)
 {
@@ -67,7 +77,19 @@ static void resolve(int dtype, int64_t M, int64_t N, int64_t K, int& variant, in
         const bool fits4 = M % 256 == 0 && N % 256 == 0 && K % bk4 == 0 && K * elt >= 2048;
         const int64_t n4 = (M / 256) * (N / 256);
         const int64_t n1 = ((M + 127) / 128) * ((N + 255) / 256);
-        tile = (fits4 && n4 >= kCus) ? 4 : n1 >= kCus ? 1 : 3;
+        const int64_t n2 = ((M + 255) / 256) * ((N + 255) / 256);
+        if (fits4 && n4 >= kCus) {
+            tile = 4;
+        } else if (n1 < kCus) {
+            tile = 3;
+        } else {
+            const int64_t load2 = (n2 + kCus - 1) / kCus;  // 256 x 256 tiles on the busiest CU
+            const int64_t c1 = (n1 + kCus - 1) / kCus;     // 128 x 256 tiles on the busiest CU
+            const bool deep = K * elt >= 2048, mid = K * elt >= 1024;
+            // load2 <= (c1 / 2) / 0.9
+            const bool big = mid && (deep || load2 == 1) && 9 * load2 <= 5 * c1;
+            tile = big ? 2 : 1;
+        }
     }
     if (variant == V_AUTO) variant = V_DIRECT;
     if (stages == 0)

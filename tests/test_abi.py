@@ -148,6 +148,30 @@ def test_pages_tile_plan(L):
     assert pi.grid == 512 and pi.k_tiles == 128
 
 
+# ---- the library's choice (AUTO) ------------------------------------------------
+@pytest.mark.parametrize("dtype,M,N,K,lay,tile,stages", [
+    (spt.F16, 4096, 4096, 4096, spt.ROW, 4, 2),     # exact 256 x 256, long K
+    (spt.I8, 4096, 4096, 4096, spt.COL, 4, 2),
+    (spt.BF16, 8192, 8192, 512, spt.ROW, 1, 3),     # low K: the C store decides
+    (spt.BF16, 8192, 8192, 64, spt.ROW, 1, 3),
+    (spt.F16, 256, 256, 256, spt.ROW, 3, 3),        # too few 128 x 256 tiles for the CUs
+    (spt.BF16, 4000, 3000, 1000, spt.ROW, 2, 2),    # one round of 256 x 256 tiles
+    (spt.BF16, 3000, 3000, 3000, spt.ROW, 2, 2),
+    (spt.F16, 5000, 5000, 1024, spt.ROW, 2, 2),
+    (spt.F16, 8000, 2000, 8000, spt.ROW, 2, 2),
+    (spt.I8, 4000, 3008, 4000, spt.COL, 2, 2),
+    (spt.BF16, 2000, 4000, 1000, spt.ROW, 1, 3),    # 256 x 256 would leave half the CUs idle
+    (spt.F16, 4100, 4100, 4100, spt.ROW, 1, 3),     # ... or a long partial round
+    (spt.F16, 6000, 6000, 2000, spt.ROW, 1, 3),
+])
+def test_auto_choice(L, dtype, M, N, K, lay, tile, stages):
+    """AUTO's tile and ring depth on shapes measured on MI355X (the comment above
+    resolve() in csrc/spt_api.cpp gives the measurements)."""
+    rc, pi = spt.spt_plan(dtype, M, N, K, lay)
+    assert rc == 0, spt.spt_last_error()
+    assert (pi.tile_id, pi.variant, pi.stages) == (tile, spt.VARIANT_DIRECT, stages)
+
+
 # ---- the persistent variant ---------------------------------------------------
 @pytest.mark.parametrize("K,window", [(64, 2), (128, 4), (192, 4), (256, 8), (512, 8), (4096, 8)])
 def test_persist_plan(L, K, window):
