@@ -308,6 +308,17 @@ def test_full_bf16_lowk(oracle_mod, K):
     sampled(oracle_mod, I.w_bf16_lowk(K))
 
 
+@pytest.mark.parametrize("w", [I.Workload("bf16 GEMM 3000x3000x3000", 31, "bf16", 3000, 3000, 3000),
+                               I.Workload("int8 GEMM 4000x3008x4000, B column-major", 32, "i8", 4000, 3008, 4000,
+                                          True)], ids=["bf16_3000", "i8_4000x3008"])
+def test_full_auto_large_tile_shapes(oracle_mod, w):
+    """Shapes on which the library's choice is the 8-wave 256 x 256 tile (general
+    kernel: edges and a K tail): sampled outputs against the oracle, int8 bit-exact."""
+    rc, pi = spt.spt_plan(spt.DTYPE_CODES[w.dtype], w.M, w.N, w.K, spt.COL if w.b_col else spt.ROW)
+    assert rc == 0 and pi.tile_id == 2
+    sampled(oracle_mod, w)
+
+
 @pytest.mark.parametrize("variant,stages", [("auto", 0), ("reg", 2), ("sync", 1)])
 def test_full_bf16_ragged(oracle_mod, variant, stages):
     sampled(oracle_mod, I.W_BF16_RAGGED, variant, stages)
