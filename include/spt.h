@@ -40,7 +40,10 @@
  * Ownership.  All matrix pointers are DEVICE pointers owned by the caller.
  * The library never allocates or frees device memory and keeps no pointer
  * after a call returns.  `stream` is a hipStream_t (NULL = the null
- * stream); the launch is asynchronous and the call never synchronizes.
+ * stream) of the calling thread's current HIP device, which must also hold
+ * the matrices; the launch is asynchronous and the call never synchronizes.
+ * SPT_ERR_LAUNCH carries the status of this call's own launch, not an error
+ * left over from earlier HIP calls.
  * The library keeps no mutable global state apart from a thread-local
  * message for spt_last_error(); concurrent calls from several threads are
  * safe.

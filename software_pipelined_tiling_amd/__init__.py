@@ -199,9 +199,10 @@ def gemm(A, B, out=None, *, b_layout: str = "row", variant: str = "auto", stages
         raise ValueError("out must be (M, >=N) with unit column stride")
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream
-    rc = spt_gemm_ex(M, N, K, A.data_ptr(), A.stride(0), B.data_ptr(), B.stride(0), out.data_ptr(),
-                     out.stride(0), d, stream, COL if col else ROW, VARIANT_CODES[variant], stages,
-                     tile)
+    with torch.cuda.device(A.device):  # the library launches on the calling thread's current device
+        rc = spt_gemm_ex(M, N, K, A.data_ptr(), A.stride(0), B.data_ptr(), B.stride(0), out.data_ptr(),
+                         out.stride(0), d, stream, COL if col else ROW, VARIANT_CODES[variant], stages,
+                         tile)
     if rc != SPT_OK:
         raise SptError(rc, "spt_gemm_ex")
     return out
@@ -223,7 +224,8 @@ def scale_by_two(x, out=None, *, stages: int = 0, blocks: int = 0, stream=None):
         raise ValueError("out must be on x's GPU")
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
-    rc = spt_scale_by_two(x.numel(), x.data_ptr(), out.data_ptr(), stages, blocks, stream)
+    with torch.cuda.device(x.device):
+        rc = spt_scale_by_two(x.numel(), x.data_ptr(), out.data_ptr(), stages, blocks, stream)
     if rc != SPT_OK:
         raise SptError(rc, "spt_scale_by_two")
     return out

@@ -9,11 +9,14 @@
 
 namespace spt {
 
+// hipLaunchKernel returns the status of this launch itself (hipGetLastError
+// would also report an error left over from an earlier, unrelated call).
 template <class C>
 hipError_t launch_gemm(const GemmArgs& a, unsigned grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL(gemm_kernel<C>, dim3(grid), dim3(C::THREADS), 0, stream, a);
-    return hipGetLastError();
+    GemmArgs arg = a;
+    void* args[] = {&arg};
+    return hipLaunchKernel((const void*)&gemm_kernel<C>, dim3(grid), dim3(C::THREADS), args, 0, stream);
 }
 
 template <int DT, int BC, int TI, int V, int S, int EX = 0>
@@ -29,8 +32,9 @@ constexpr KernelEntry entry()
 template <class C, int P>
 hipError_t launch_persist(const GemmArgs& a, unsigned grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL((gemm_persist_kernel<C, P>), dim3(grid), dim3(C::THREADS), 0, stream, a);
-    return hipGetLastError();
+    GemmArgs arg = a;
+    void* args[] = {&arg};
+    return hipLaunchKernel((const void*)&gemm_persist_kernel<C, P>, dim3(grid), dim3(C::THREADS), args, 0, stream);
 }
 
 template <int DT, int BC, int TI, int S, int P>

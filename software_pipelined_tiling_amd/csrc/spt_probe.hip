@@ -53,19 +53,12 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(const i32x4_t* ops, int
 hipError_t launch_mfma_probe(int dtype, const void* ops, int64_t n_vec, int64_t iters, float* sink,
                              hipStream_t stream)
 {
-    const dim3 grid(256), block(256);
-    switch (dtype) {
-    case DT_F16:
-        hipLaunchKernelGGL(mfma_probe_kernel<DT_F16>, grid, block, 0, stream, (const i32x4_t*)ops, n_vec, iters, sink);
-        break;
-    case DT_BF16:
-        hipLaunchKernelGGL(mfma_probe_kernel<DT_BF16>, grid, block, 0, stream, (const i32x4_t*)ops, n_vec, iters, sink);
-        break;
-    default:
-        hipLaunchKernelGGL(mfma_probe_kernel<DT_I8>, grid, block, 0, stream, (const i32x4_t*)ops, n_vec, iters, sink);
-        break;
-    }
-    return hipGetLastError();
+    const i32x4_t* o = (const i32x4_t*)ops;
+    void* args[] = {&o, &n_vec, &iters, &sink};
+    const void* k = dtype == DT_F16    ? (const void*)&mfma_probe_kernel<DT_F16>
+                    : dtype == DT_BF16 ? (const void*)&mfma_probe_kernel<DT_BF16>
+                                       : (const void*)&mfma_probe_kernel<DT_I8>;
+    return hipLaunchKernel(k, dim3(256), dim3(256), args, 0, stream);
 }
 
 }  // namespace spt

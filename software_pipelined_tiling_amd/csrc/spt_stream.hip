@@ -136,8 +136,9 @@ __global__ __launch_bounds__(kStreamThreads) void scale_by_two_kernel(StreamArgs
 template <int S>
 static hipError_t launch_stream(const StreamArgs& a, unsigned blocks, hipStream_t stream)
 {
-    hipLaunchKernelGGL(scale_by_two_kernel<S>, dim3(blocks), dim3(kStreamThreads), 0, stream, a);
-    return hipGetLastError();
+    StreamArgs arg = a;
+    void* args[] = {&arg};
+    return hipLaunchKernel((const void*)&scale_by_two_kernel<S>, dim3(blocks), dim3(kStreamThreads), args, 0, stream);
 }
 
 hipError_t launch_scale_by_two(const void* x, void* y, int64_t n, int stages, unsigned blocks, hipStream_t stream)

@@ -247,6 +247,34 @@ def test_torch_wrapper_rejects_unsafe_arguments():
     assert tuple(C.shape) == (64, 40)
 
 
+def test_launch_status_ignores_an_earlier_hip_error(oracle_mod):
+    """A failed HIP call made before spt_gemm (here an allocation of 2^50 bytes,
+    which the runtime refuses) leaves an error in the runtime's last-error slot;
+    the library reports its own launch's status, and computes C."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t]
+    hip.hipMalloc.restype = ctypes.c_int
+    hip.hipGetLastError.restype = ctypes.c_int
+    hip.hipPeekAtLastError.restype = ctypes.c_int
+    A, B = operands("f16", False, 128, 256, 64, 9, pad_nan=False)
+    dA, dB = to_dev(A, "f16"), to_dev(B, "f16")
+    C = alloc_c(128, 256, "f16")
+    torch.cuda.synchronize()
+    p = ctypes.c_void_p()
+    try:
+        assert hip.hipMalloc(ctypes.byref(p), 1 << 50) != 0
+        assert hip.hipPeekAtLastError() != 0
+        rc = spt.spt_gemm(128, 256, 64, dA.data_ptr(), A.shape[1], dB.data_ptr(), B.shape[1], C.data_ptr(),
+                          C.stride(0), spt.F16, torch.cuda.current_stream().cuda_stream)
+        assert rc == spt.SPT_OK, spt.spt_last_error()
+    finally:
+        hip.hipGetLastError()  # clear the slot for later tests
+    torch.cuda.synchronize()
+    parity.check_full(C.cpu().numpy(), ref(oracle_mod, A, B, "f16", False, 256, 64), A, B, "f16", False,
+                      128, 256, 64)
+
+
 # ---------------------------------------------------------------------------
 # Full-size workloads, in the launch configurations the benchmark times;
 # sampled outputs are recomputed one by one by the oracle.
