@@ -21,7 +21,7 @@ counts.  `check(kernel)` turns that into pass/fail properties:
 
   DIRECT ring (buffer_load ... lds into an S-stage ring):
     counts     MFMAs, copies and barriers per iteration match the plan
-    vmcnt      every vmcnt wait in the loop is (S-2) x copies-per-tile: the
+    vmcnt      one vmcnt wait per tile, each (S-2) x copies-per-tile: the
                copies of younger tiles stay in flight (for S >= 3 there is
                no vmcnt(0) in the steady state)
     lgkmcnt    one lgkmcnt(0) per tile (before the barrier); every other
@@ -392,7 +392,7 @@ def check(k: Kernel) -> Dict[str, bool]:
     if k.variant == "direct":
         res["counts"] = (st["mfma"] == T * g["mfma_per_tile"] and st["dma"] == T * g["loads_per_tile"]
                          and st["barriers"] == T)
-        res["vmcnt"] = bool(st["vmcnt_waits"]) and all(
+        res["vmcnt"] = len(st["vmcnt_waits"]) == T and all(
             v == (k.stages - 2) * g["loads_per_tile"] for v in st["vmcnt_waits"])
         res["lgkmcnt"] = st["lgkmcnt_waits"].count(0) == T
         # each copy in an MFMA gap of its own, none in the gap of the barrier, fragment

@@ -9,6 +9,7 @@ plan ("Pipeline GPU Kernel", Schritt 4: check in the generated code that the
 next tile's loads are in flight during the math of the current one).
 """
 import os
+import re
 import shutil
 
 import pytest
@@ -133,3 +134,54 @@ def test_persistent_ring_schedule(built_lib):
     for k in ks:
         res = X.check_persist(k)
         assert all(res.values()), (k.name, res, X.persist_stats(k))
+
+
+# ---- the checks see the mistakes the pages warn about ---------------------------------
+def _planted(k, edits):
+    """Copy of kernel k with instruction i's operation replaced by op, for each (i, op)."""
+    import dataclasses
+    ins = list(k.instrs)
+    for i, op in edits:
+        ins[i] = ins[i].split("|", 1)[0] + "|" + op
+    return dataclasses.replace(k, instrs=ins)
+
+
+def _ops(k):
+    return [x.split("|", 1)[1] for x in k.instrs]
+
+
+def _is_dma(op):
+    return op.startswith("buffer_load") and op.rstrip().endswith("lds")
+
+
+@pytest.mark.parametrize("tile,stages", [(4, 2), (1, 3)])
+def test_checks_catch_planted_schedule_faults(kernels, tile, stages):
+    """Each fault is planted in a copy of the shipped exact-fit DIRECT kernel's
+    disassembly (on the CPU; no broken kernel is ever run): the steady loop's
+    barrier removed; its vmcnt wait removed, loosened or tightened to 0 (an
+    early wait); one copy dropped; the lgkmcnt(0) before the barrier loosened;
+    a copy moved beside the barrier.  check() passes the real kernel and fails
+    every planted one ("Pipeline GPU Kernel", Haeufige Stolperfallen: missing
+    barriers, swapped commit/wait, a forgotten epilogue tile)."""
+    (k,) = pick(kernels, dtype=0, bcol=False, tile=tile, variant="direct", stages=stages, exact=True)
+    assert all(X.check(k).values())
+    ops = _ops(k)
+    bar = max(i for i, o in enumerate(ops) if o.startswith("s_barrier"))  # the steady loop's barrier
+    vm = max(i for i in range(bar) if re.search(r"vmcnt\(\d+\)", ops[i]))
+    lg = max(i for i in range(bar) if ops[i].startswith("s_waitcnt lgkmcnt(0)"))
+    last_dma = max(i for i, o in enumerate(ops) if _is_dma(o))
+    dma_after = min(i for i in range(bar + 1, len(ops)) if _is_dma(ops[i]))
+    want = int(re.search(r"vmcnt\((\d+)\)", ops[vm]).group(1))
+    planted = {
+        "no barrier": ([(bar, "s_nop 0")], "counts"),
+        "no wait": ([(vm, "s_nop 0")], "vmcnt"),
+        "wait too loose": ([(vm, f"s_waitcnt vmcnt({want + 1})")], "vmcnt"),
+        "copy dropped": ([(last_dma, "s_nop 0")], "counts"),
+        "fragment reads not drained": ([(lg, "s_waitcnt lgkmcnt(1)")], "lgkmcnt"),
+        "copy beside the barrier": ([(bar + 1, ops[dma_after]), (dma_after, ops[bar + 1])], "overlap"),
+    }
+    if want > 0:
+        planted["early wait"] = ([(vm, "s_waitcnt vmcnt(0)")], "vmcnt")
+    for name, (edits, prop) in planted.items():
+        res = X.check(_planted(k, edits))
+        assert not res[prop], (name, res)
