@@ -247,7 +247,7 @@ def check_persist(k: PersistKernel) -> Dict[str, bool]:
     return {
         "counts": (st["mfma"] == 2 * g["mfma_per_tile"] and st["dma"] == 2 * L and st["stores"] == 2 * ST
                    and st["barriers"] == 2),
-        "vmcnt": bool(st["vmcnt_waits"]) and all(v == steady for v in st["vmcnt_waits"]),
+        "vmcnt": len(st["vmcnt_waits"]) == 2 and all(v == steady for v in st["vmcnt_waits"]),
         "kernel_vmcnt": set(st["kernel_vmcnt_waits"]) <= {steady, first, 0},
         "order": st["copies_before_stores"],
         "clean": st["scratch"] == 0 and st["acc_moves"] == 0,
