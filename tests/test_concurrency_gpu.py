@@ -1,0 +1,117 @@
+"""Concurrent calls and captured launches of the GEMM, on an MI355X.
+
+Between calls the library keeps only a thread-local error message, so calls
+from several host threads, each on its own stream, must each give the C of a
+single call.  A call is one kernel launch with no allocation, copy or memset,
+so it can also be captured into a HIP graph: every replay must give the C of
+an eager call on the operands the buffers hold at that moment.
+"""
+from __future__ import annotations
+
+import threading
+
+import numpy as np
+import pytest
+
+import software_pipelined_tiling_amd as spt
+from tests import parity
+from tests.test_gemm_gpu import alloc_c, operands, ref, run, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu(built_lib):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    spt.lib()
+
+
+def test_threads_on_their_own_streams(oracle_mod):
+    """Four host threads, eight calls each, on four streams into four outputs:
+    every output bit-identical to one call's C, which matches the oracle."""
+    M, N, K = 384, 512, 320
+    A, B = operands("bf16", False, M, N, K, 61, pad_nan=False)
+    expect = run(A, B, "bf16", False, M, N, K)
+    parity.check_full(expect, ref(oracle_mod, A, B, "bf16", False, N, K), A, B, "bf16", False, M, N, K)
+    dA, dB = to_dev(A, "bf16"), to_dev(B, "bf16")
+    nthreads, reps = 4, 8
+    outs = [alloc_c(M, N, "bf16") for _ in range(nthreads)]
+    streams = [torch.cuda.Stream() for _ in range(nthreads)]
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(i):
+        for r in range(reps):
+            rc = spt.spt_gemm_ex(M, N, K, dA.data_ptr(), A.shape[1], dB.data_ptr(), B.shape[1], outs[i].data_ptr(),
+                                 N, spt.BF16, streams[i].cuda_stream, spt.ROW, spt.VARIANT_AUTO, 0, 0)
+            if rc != spt.SPT_OK:
+                errors.append((i, r, spt.spt_status_string(rc), spt.spt_last_error()))
+
+    print(f"[gpu] {nthreads} threads x {reps} calls, bf16 {M}x{N}x{K}", flush=True)
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(nthreads)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for o in outs:
+        assert np.array_equal(o.cpu().numpy().view(np.uint32), expect.view(np.uint32))
+
+
+def test_errors_stay_with_their_thread():
+    """A refused call on one thread sets that thread's message only."""
+    assert spt.spt_gemm(1, 1, 1, 0, 1, 0, 1, 0, 1, 9, 0) == spt.SPT_ERR_INVALID
+    assert "dtype 9" in spt.spt_last_error()
+    msgs = {}
+
+    def bad():
+        assert spt.spt_gemm(-1, 1, 1, 0, 1, 0, 1, 0, 1, spt.F16, 0) == spt.SPT_ERR_INVALID
+        msgs["bad"] = spt.spt_last_error()
+
+    t = threading.Thread(target=bad)
+    t.start()
+    t.join()
+    assert "negative" in msgs["bad"]
+    assert "dtype 9" in spt.spt_last_error()
+
+
+@pytest.mark.parametrize("dtype,b_col", [("f16", False), ("i8", True)])
+def test_captured_in_a_hip_graph(oracle_mod, dtype, b_col):
+    """One call captured into a graph, replayed six times over two operand sets
+    that eager copies swap in between replays (C reset to a sentinel each time):
+    every replay bit-identical to the eager call on the same operands."""
+    M, N, K = 256, 384, 512
+    sets = [operands(dtype, b_col, M, N, K, 71 + i, pad_nan=False) for i in range(2)]
+    eager = [run(A, B, dtype, b_col, M, N, K, ldc_pad=0) for A, B in sets]
+    for (A, B), C in zip(sets, eager):
+        parity.check_full(C, ref(oracle_mod, A, B, dtype, b_col, N, K), A, B, dtype, b_col, M, N, K)
+    A0, B0 = sets[0]
+    dA, dB = to_dev(A0, dtype), to_dev(B0, dtype)
+    C = alloc_c(M, N, dtype)
+    layout = "col" if b_col else "row"
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # a first call outside the capture
+        spt.gemm(dA, dB, out=C, b_layout=layout)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    print(f"[gpu] capture {dtype} {layout} {M}x{N}x{K}", flush=True)
+    with torch.cuda.graph(g):
+        spt.gemm(dA, dB, out=C, b_layout=layout)
+    torch.cuda.synchronize()
+    sentinel = alloc_c(M, N, dtype)
+    for i in range(6):
+        A, B = sets[i % 2]
+        dA.copy_(to_dev(A, dtype))
+        dB.copy_(to_dev(B, dtype))
+        C.copy_(sentinel)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = C.cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), eager[i % 2].view(np.uint32)), f"replay {i}"
