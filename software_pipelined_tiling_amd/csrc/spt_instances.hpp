@@ -60,8 +60,13 @@ constexpr KernelEntry pentry()
 #define SPT_RING3(DT, BC, TI) entry<DT, BC, TI, V_DIRECT, 3>()
 #define SPT_RING34(DT, BC, TI) entry<DT, BC, TI, V_DIRECT, 3>(), entry<DT, BC, TI, V_DIRECT, 4>()
 
-// Exact-fit instantiations of the ring variants (no K tail, no edge checks).
-#define SPT_EXACT(DT, BC, TI) entry<DT, BC, TI, V_DIRECT, 2, 1>()
+// Exact-fit instantiations (no K tail, no edge checks) of every (variant, stages) pair: the
+// unpipelined and register-staged loops are compared with the ring in the same form.  (The
+// general 256 x 256 kernels spill: their edge and tail code needs registers the 256
+// accumulators of a 128 x 128 wave tile leave no room for.)
+#define SPT_EXACT(DT, BC, TI)                                                                    \
+    entry<DT, BC, TI, V_SYNC, 1, 1>(), entry<DT, BC, TI, V_REG, 1, 1>(), entry<DT, BC, TI, V_REG, 2, 1>(), \
+        entry<DT, BC, TI, V_DIRECT, 2, 1>()
 #define SPT_EXACT34(DT, BC, TI) entry<DT, BC, TI, V_DIRECT, 3, 1>(), entry<DT, BC, TI, V_DIRECT, 4, 1>()
 
 #define SPT_TILE_ALL(DT, BC, TI) SPT_PAIRS(DT, BC, TI), SPT_RING34(DT, BC, TI), SPT_EXACT(DT, BC, TI), SPT_EXACT34(DT, BC, TI)

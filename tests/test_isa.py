@@ -34,9 +34,10 @@ def pick(ks, **kw):
 
 
 def test_every_built_entry_is_in_the_binary(kernels):
-    # 8 tables (element type x B layout) of 34: SYNC, REG 1/2 and DIRECT 2 on every
-    # tile, DIRECT 3/4 where the ring fits in LDS, exact-fit forms of tiles 1, 2, 4, 5
-    assert len(kernels) == 8 * 34
+    # 8 tables (element type x B layout) of 46: SYNC, REG 1/2 and DIRECT 2 on every tile,
+    # DIRECT 3/4 where the ring fits in LDS (tiles 1, 3, 5), and exact-fit forms of all
+    # of these on tiles 1, 2, 4 and 5
+    assert len(kernels) == 8 * 46
     assert {k.tile for k in kernels} == {1, 2, 3, 4, 5}
 
 
@@ -185,3 +186,29 @@ def test_checks_catch_planted_schedule_faults(kernels, tile, stages):
     for name, (edits, prop) in planted.items():
         res = X.check(_planted(k, edits))
         assert not res[prop], (name, res)
+
+
+# The kernels the library's own choice runs, and the exact-fit forms that the pipelining
+# comparisons time (every (variant, stages) pair of a tile in the same form as its ring).
+AUTO_CHOICES = {(1, "direct", 3), (2, "direct", 2), (3, "direct", 3), (4, "direct", 2)}
+COMPARED = {("sync", 1), ("reg", 1), ("reg", 2), ("direct", 2)}
+
+
+def test_default_and_compared_kernels_keep_scratch_out_of_the_loop(kernels):
+    """No scratch access in the steady loop of any kernel AUTO can select (the 256 x 256
+    one-wave-per-SIMD tile only in its exact-fit form, as the planner selects it) or of the
+    exact-fit forms the pipelining comparisons use.  Only the general int8 row-major-B
+    8-wave kernel spills at all (2 registers, outside its loop)."""
+    seen = 0
+    for k in kernels:
+        auto = (k.tile, k.variant, k.stages) in AUTO_CHOICES and (k.tile != 4 or k.exact)
+        compared = k.exact and k.tile in (1, 2, 4, 5) and (k.variant, k.stages) in COMPARED
+        if not (auto or compared):
+            continue
+        seen += 1
+        assert X.loop_stats(k)["scratch"] == 0, k.name
+        if not (k.dtype == 2 and not k.bcol and k.tile == 2 and not k.exact):
+            assert k.meta["vgpr_spill"] == 0 and k.meta["scratch"] == 0, (k.name, k.meta)
+    # per table: 6 selectable (tiles 1 and 2 in both forms, 3 general, 4 exact) and 16 compared,
+    # 2 of them in both sets
+    assert seen == 8 * (6 + 16 - 2)
