@@ -16,7 +16,7 @@
 //            register-only prefetch of Schritt 1) or S = 2 (double buffer).
 //  V_DIRECT  asynchronous global -> LDS copies (the pages' cp.async, on CDNA4
 //            buffer_load_dwordx4 ... lds, which writes LDS without a VGPR
-//            round trip) into an S-stage ring, S = 2 or 3 (sections 5, 6),
+//            round trip) into an S-stage ring, S = 2, 3 or 4 (sections 5, 6),
 //            with a second, register-level pipeline of LDS -> VGPR fragment
 //            reads (section 7).
 //
