@@ -384,3 +384,16 @@ def test_large_output_sampled(oracle_mod):
     """C of 16384 x 16384 fp32 (1 GiB) from K = 64: every output written, sampled
     entries against the oracle."""
     sampled(oracle_mod, I.Workload("fp16 GEMM 16384x16384x64", 23, "f16", 16384, 16384, 64), n=2000)
+
+
+@pytest.mark.parametrize("dtype,b_col", [("bf16", False), ("i8", True), ("f32", False)])
+@pytest.mark.parametrize("M,N,K", [(1, 70001, 300), (70001, 1, 300), (3, 5, 100003), (129, 40000, 40)])
+def test_extreme_aspect_ratios(oracle_mod, dtype, b_col, M, N, K):
+    """One row or one column of C across hundreds of tiles, a tiny C from a K of
+    10^5 (thousands of K tiles and a ragged tail), and a wide C from a short K:
+    full C against the oracle, under AUTO and the unpipelined loop."""
+    A, B = operands(dtype, b_col, M, N, K, 300 + M % 97 + N % 89, lda_pad=1, ldb_pad=2)
+    Cref = ref(oracle_mod, A, B, dtype, b_col, N, K)
+    for v, s in (("auto", 0), ("sync", 1)):
+        C = run(A, B, dtype, b_col, M, N, K, v, s)
+        parity.check_full(C, Cref, A, B, dtype, b_col, M, N, K)
