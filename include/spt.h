@@ -223,7 +223,8 @@ int spt_scale_by_two(int64_t n, const void* x, void* y, int stages, int blocks, 
 /* Static string naming a status code. */
 const char* spt_status_string(int status);
 
-/* Thread-local detail of the last failing call on this thread ("" if none). */
+/* Thread-local detail of this thread's most recent call to the entry points
+ * above: a message if it failed, "" if it returned SPT_OK or none was made. */
 const char* spt_last_error(void);
 
 /* SPT_VERSION of the loaded library. */

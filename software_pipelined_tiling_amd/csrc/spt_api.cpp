@@ -277,7 +277,6 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     a.k_tail = pi.k_tail;
     const hipError_t err = e->launch(a, (unsigned)pi.grid, (hipStream_t)stream);
     if (err != hipSuccess) return fail(SPT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(err));
-    g_last_error[0] = 0;
     return SPT_OK;
 }
 
@@ -306,7 +305,6 @@ static int scale_by_two_impl(int64_t n, const void* x, void* y, int stages, int 
     const int64_t g = want < tiles ? want : tiles;
     const hipError_t err = launch_scale_by_two(x, y, n, s, (unsigned)g, (hipStream_t)stream);
     if (err != hipSuccess) return fail(SPT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(err));
-    g_last_error[0] = 0;
     return SPT_OK;
 }
 
@@ -319,8 +317,15 @@ static int mfma_probe_impl(int dtype, const void* ops, int64_t bytes, int64_t it
     if ((uintptr_t)ops % 16) return fail(SPT_ERR_MISALIGNED, "operands not 16-byte aligned");
     const hipError_t err = launch_mfma_probe(dtype, ops, bytes / 16, iters, (float*)sink, (hipStream_t)stream);
     if (err != hipSuccess) return fail(SPT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(err));
-    g_last_error[0] = 0;
     return SPT_OK;
+}
+
+// Every entry point returns through here: the thread's message describes its
+// most recent call, and is empty when that call succeeded.
+static int done(int status)
+{
+    if (status == SPT_OK) g_last_error[0] = 0;
+    return status;
 }
 
 }  // namespace spt
@@ -329,36 +334,36 @@ extern "C" {
 
 int spt_probe_mfma(int dtype, const void* operands, int64_t operand_bytes, int64_t iters, void* sink, void* stream)
 {
-    return spt::mfma_probe_impl(dtype, operands, operand_bytes, iters, sink, stream);
+    return spt::done(spt::mfma_probe_impl(dtype, operands, operand_bytes, iters, sink, stream));
 }
 
 
 int spt_scale_by_two(int64_t n, const void* x, void* y, int stages, int blocks, void* stream)
 {
-    return spt::scale_by_two_impl(n, x, y, stages, blocks, stream);
+    return spt::done(spt::scale_by_two_impl(n, x, y, stages, blocks, stream));
 }
 
 
 int spt_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
              void* C, int64_t ldc, int dtype, void* stream)
 {
-    return spt::gemm_impl(M, N, K, A, lda, B, ldb, C, ldc, dtype, stream, SPT_ROW, SPT_VARIANT_AUTO, 0,
-                          SPT_TILE_AUTO);
+    return spt::done(spt::gemm_impl(M, N, K, A, lda, B, ldb, C, ldc, dtype, stream, SPT_ROW, SPT_VARIANT_AUTO, 0,
+                                    SPT_TILE_AUTO));
 }
 
 int spt_gemm_ex(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
                 void* C, int64_t ldc, int dtype, void* stream, int b_layout, int variant, int stages,
                 int tile_id)
 {
-    return spt::gemm_impl(M, N, K, A, lda, B, ldb, C, ldc, dtype, stream, b_layout, variant, stages,
-                          tile_id);
+    return spt::done(spt::gemm_impl(M, N, K, A, lda, B, ldb, C, ldc, dtype, stream, b_layout, variant, stages,
+                                    tile_id));
 }
 
 int spt_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, int variant, int stages,
              int tile_id, spt_plan_info* out)
 {
     if (!out) return spt::fail(SPT_ERR_INVALID, "out is null");
-    return spt::make_plan(dtype, M, N, K, b_layout, variant, stages, tile_id, out);
+    return spt::done(spt::make_plan(dtype, M, N, K, b_layout, variant, stages, tile_id, out));
 }
 
 const char* spt_status_string(int status)

@@ -243,3 +243,19 @@ def test_panel_above_2gib_is_refused(L):
     K = 1 << 22
     assert ex(M=256, N=256, K=K, lda=K, tile=spt.TILE_256x256_4W) == -2
     assert "2 GiB" in spt.spt_last_error()
+
+
+def test_last_error_describes_the_most_recent_call():
+    """spt_last_error() holds a message after a refused call and is empty after any
+    call that returned SPT_OK, including calls with nothing to launch."""
+    assert spt.spt_plan(9, 64, 64, 64)[0] == spt.SPT_ERR_INVALID
+    assert "dtype 9" in spt.spt_last_error()
+    assert spt.spt_plan(spt.F16, 64, 64, 64)[0] == spt.SPT_OK
+    assert spt.spt_last_error() == ""
+    assert spt.spt_gemm(-1, 1, 1, 0, 1, 0, 1, 0, 1, spt.F16, 0) == spt.SPT_ERR_INVALID
+    assert spt.spt_last_error() != ""
+    assert spt.spt_gemm(0, 64, 64, 0, 64, 0, 64, 0, 64, spt.F16, 0) == spt.SPT_OK  # M = 0: no launch
+    assert spt.spt_last_error() == ""
+    assert spt.spt_scale_by_two(-1, 0, 0) == spt.SPT_ERR_INVALID
+    assert spt.spt_scale_by_two(0, 0, 0) == spt.SPT_OK
+    assert spt.spt_last_error() == ""
