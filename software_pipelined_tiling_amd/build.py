@@ -37,6 +37,13 @@ def _compile(src: str, defines=(), tag: str = "") -> str:
     return obj
 
 
+def build_all(verbose: bool = True) -> None:
+    """libspt.so and the race-detection libspt_poison.so, compiled side by side."""
+    with cf.ThreadPoolExecutor(max_workers=2) as ex:
+        for f in [ex.submit(build, verbose=verbose), ex.submit(build_poison, verbose=verbose)]:
+            f.result()
+
+
 def build(jobs: int | None = None, verbose: bool = True, defines=(), out: str | None = None,
           reuse: bool = False, only=()) -> str:
     """Compile every source for gfx950 and link libspt.so (or `out`); returns its path.
@@ -67,6 +74,42 @@ def build(jobs: int | None = None, verbose: bool = True, defines=(), out: str | 
     return lib
 
 
+POISON_LIB = os.path.join(HERE, "libspt_poison.so")
+POISON_TABLES = ("f16_row", "i8_col")
+
+
+def build_poison(verbose: bool = True) -> str:
+    """The race-detection library ``libspt_poison.so``: the same C ABI, built with
+    SPT_POISON, so that every ring refills a freed stage only after poisoning it.
+    It holds the kernel tables of fp16 with row-major B and int8 with column-major B;
+    the other element types and layouts have empty tables (SPT_ERR_UNSUPPORTED).
+    Test infrastructure: the product loads libspt.so only."""
+    os.makedirs(BUILD, exist_ok=True)
+    stub = os.path.join(BUILD, "spt_poison_stub.cpp")
+    empty = [f"{dt}_{lay}" for dt in ("f16", "bf16", "i8", "f32") for lay in ("row", "col")
+             if f"{dt}_{lay}" not in POISON_TABLES]
+    with open(stub, "w") as f:
+        f.write('#include "spt_registry.h"\nnamespace spt {\n')
+        f.writelines(f"KernelTable kernels_{t}() {{ return KernelTable{{nullptr, 0}}; }}\n" for t in empty)
+        f.write("}\n")
+    srcs = [f"spt_kernels_{t}.hip" for t in POISON_TABLES] + ["spt_stream.hip", "spt_probe.hip", "spt_api.cpp"]
+    with cf.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, ("SPT_POISON",), "_poison"), srcs))
+    stub_obj = os.path.join(BUILD, "spt_poison_stub.o")
+    r = subprocess.run([HIPCC, *COMMON, "-I", CSRC, "-c", stub, "-o", stub_obj], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the poison stub:\n{r.stderr[-4000:]}")
+    tmp = POISON_LIB + ".tmp"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, stub_obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr[-4000:]}")
+    os.replace(tmp, POISON_LIB)
+    if verbose:
+        print(f"built {POISON_LIB}", file=sys.stderr)
+    return POISON_LIB
+
+
 def asm(src: str = "spt_kernels_f16_row.hip", out: str | None = None) -> str:
     """gfx950 assembly of one kernel translation unit (for the ISA checks)."""
     os.makedirs(BUILD, exist_ok=True)
@@ -79,4 +122,4 @@ def asm(src: str = "spt_kernels_f16_row.hip", out: str | None = None) -> str:
 
 
 if __name__ == "__main__":
-    build()
+    build_all()

@@ -72,11 +72,22 @@ constexpr KernelEntry pentry()
 #define SPT_TILE_ALL(DT, BC, TI) SPT_PAIRS(DT, BC, TI), SPT_RING34(DT, BC, TI), SPT_EXACT(DT, BC, TI), SPT_EXACT34(DT, BC, TI)
 #define SPT_TILE_BIG(DT, BC, TI) SPT_PAIRS(DT, BC, TI), SPT_EXACT(DT, BC, TI)
 
-// The table of one (element type, B layout): NAME is e.g. f16_row.
+// The table of one (element type, B layout): NAME is e.g. f16_row.  Race-detection
+// builds (SPT_POISON) hold the ring kernels only: DIRECT on every tile and PERSIST.
+#ifdef SPT_POISON
+#define SPT_RING_ONLY(DT, BC, TI) entry<DT, BC, TI, V_DIRECT, 2>(), entry<DT, BC, TI, V_DIRECT, 2, 1>()
+#define SPT_TABLE_ENTRIES(DT, BC)                                                                      \
+    SPT_RING_ONLY(DT, BC, 1), SPT_RING34(DT, BC, 1), SPT_EXACT34(DT, BC, 1), SPT_RING_ONLY(DT, BC, 2),   \
+        entry<DT, BC, 3, V_DIRECT, 2>(), SPT_RING34(DT, BC, 3), SPT_RING_ONLY(DT, BC, 4),               \
+        SPT_RING_ONLY(DT, BC, 5), SPT_RING34(DT, BC, 5), SPT_EXACT34(DT, BC, 5), SPT_PERSIST(DT, BC)
+#else
+#define SPT_TABLE_ENTRIES(DT, BC)                                                                      \
+    SPT_TILE_ALL(DT, BC, 1), SPT_TILE_BIG(DT, BC, 2), SPT_PAIRS(DT, BC, 3), SPT_RING34(DT, BC, 3),      \
+        SPT_TILE_BIG(DT, BC, 4), SPT_TILE_ALL(DT, BC, 5), SPT_PERSIST(DT, BC)
+#endif
 #define SPT_DEFINE_TABLE(NAME, DT, BC)                                                          \
     static const KernelEntry k_##NAME[] = {                                                    \
-        SPT_TILE_ALL(DT, BC, 1), SPT_TILE_BIG(DT, BC, 2), SPT_PAIRS(DT, BC, 3), SPT_RING34(DT, BC, 3), \
-        SPT_TILE_BIG(DT, BC, 4), SPT_TILE_ALL(DT, BC, 5), SPT_PERSIST(DT, BC),                 \
+        SPT_TABLE_ENTRIES(DT, BC),                                                             \
     };                                                                                         \
     KernelTable kernels_##NAME() { return KernelTable{k_##NAME, (int)(sizeof(k_##NAME) / sizeof(k_##NAME[0]))}; }
 

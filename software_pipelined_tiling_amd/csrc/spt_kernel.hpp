@@ -531,6 +531,28 @@ struct Gemm {
         }
     }
 
+#ifdef SPT_POISON
+    // Race-detection builds only (never in the shipped library): after the barrier
+    // that frees a stage, fill the 1 KiB blocks this wave's copies are about to
+    // refill with a poison pattern (NaN for the float types, 127 for int8) and wait
+    // for those writes before the copies are issued.  A read of the stage before its
+    // copies land then shows up in C as NaN, or as a wrong int8 sum.
+    static __device__ __forceinline__ void poison(const Ring& r, uint32_t stage_off)
+    {
+        constexpr int pv = C::DT == DT_F16 ? 0x7E007E00 : C::DT == DT_BF16 ? 0x7FC07FC0
+                           : C::DT == DT_F32 ? 0x7FC00000 : 0x7F7F7F7F;
+        const i32x4_t v = {pv, pv, pv, pv};
+        const uint32_t lane = (threadIdx.x & 63) * 16;
+#pragma unroll
+        for (int i = 0; i < C::A_CPT; ++i)
+            *(SPT_LDS i32x4_t*)(size_t)(r.m0a + stage_off + i * 1024 + lane) = v;
+#pragma unroll
+        for (int i = 0; i < C::B_CPT; ++i)
+            *(SPT_LDS i32x4_t*)(size_t)(r.m0b + stage_off + i * 1024 + lane) = v;
+        wait_lgkmcnt0();
+    }
+#endif
+
     // The copies of one K tile into one stage: copy j < A_CPT of the wave moves
     // A block j of its run of A_CPT blocks, copy A_CPT + i B block i.
     struct Dma {
@@ -874,6 +896,9 @@ struct Gemm {
                 wait_vmcnt<(C::S - 2) * C::LOADS>();   // its copies of the next tile have landed
                 barrier();                             // next tile visible to all; this stage free
                 const Dma d = dma_of(r, rs);           // tile + S into this stage
+#ifdef SPT_POISON
+                poison(r, rs);
+#endif
                 step<C::LOADS, true, true>(use, nxt, smem + nx, L, 0, d, cp, r, acc);
             }
         });

@@ -226,6 +226,9 @@ struct Persist {
         wait_vmcnt<VM_STEADY>();     // its copies of the next K tile have landed
         barrier();                   // next K tile visible to all; this stage free
         const typename G::Dma d = G::dma_of(q.r, rs);
+#ifdef SPT_POISON
+        G::poison(q.r, rs);
+#endif
         kstep<FIRST, SB>(sl[PAR], sl[PAR ^ 1], smem + nx, L, d, cp, p, q, acc, out, crs, vc);
         rs = nx;
     }

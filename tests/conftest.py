@@ -26,3 +26,12 @@ def built_lib():
     if not os.path.exists(b.LIB):
         b.build()
     return b.LIB
+
+
+@pytest.fixture(scope="session")
+def poison_lib():
+    """libspt_poison.so (the race-detection build) as built in-tree; built here only when it is missing."""
+    from software_pipelined_tiling_amd import build as b
+    if not os.path.exists(b.POISON_LIB):
+        b.build_poison()
+    return b.POISON_LIB
