@@ -44,7 +44,7 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "i8": 5033.2, "f32": 157.3}  # dense MFMA, MI355X
 HBM_GBS = 8000.0
 PAIRS = [("sync", 1), ("reg", 1), ("reg", 2), ("direct", 2), ("direct", 3), ("direct", 4)]
-TILES = (1, 2, 3, 4, 5)
+TILES = (1, 2, 3, 4, 5, 6)
 FLOP_PER_CLK = {"f16": 256 * 4096, "bf16": 256 * 4096, "i8": 256 * 8192}  # dense MFMA, whole chip
 
 

@@ -124,6 +124,9 @@ enum spt_variant {
  *                    waves of 128 x 128, one wave per SIMD).
  *  SPT_TILE_256x256_4W_K64B  the same with a 64-byte K depth (room for a
  *                    3- or 4-stage ring).
+ *  SPT_TILE_256x192  256 x 192, 128-byte K depth, 512 threads (2 x 4 waves
+ *                    of 128 x 48): fills a round of CUs that the 256 x 256
+ *                    grid of a shape would leave partly idle.
  */
 enum spt_tile {
     SPT_TILE_AUTO = 0,
@@ -131,7 +134,8 @@ enum spt_tile {
     SPT_TILE_256x256 = 2,
     SPT_TILE_128x128 = 3,
     SPT_TILE_256x256_4W = 4,
-    SPT_TILE_256x256_4W_K64B = 5
+    SPT_TILE_256x256_4W_K64B = 5,
+    SPT_TILE_256x192 = 6
 };
 
 enum spt_status {

@@ -18,7 +18,7 @@ __all__ = [
     "spt_scale_by_two", "spt_probe_mfma", "gemm", "plan", "scale_by_two", "SptError", "PlanInfo", "lib_path",
     "F16", "BF16", "I8", "F32", "ROW", "COL", "VARIANT_AUTO", "VARIANT_SYNC", "VARIANT_REG",
     "VARIANT_DIRECT", "VARIANT_PERSIST", "TILE_AUTO", "TILE_128x256", "TILE_256x256", "TILE_128x128", "TILE_256x256_4W",
-    "TILE_256x256_4W_K64B",
+    "TILE_256x256_4W_K64B", "TILE_256x192",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,7 +28,8 @@ lib_path = os.path.join(HERE, "libspt.so")
 F16, BF16, I8, F32 = 0, 1, 2, 3
 ROW, COL = 0, 1
 VARIANT_AUTO, VARIANT_SYNC, VARIANT_REG, VARIANT_DIRECT, VARIANT_PERSIST = 0, 1, 2, 3, 4
-TILE_AUTO, TILE_128x256, TILE_256x256, TILE_128x128, TILE_256x256_4W, TILE_256x256_4W_K64B = 0, 1, 2, 3, 4, 5
+TILE_AUTO, TILE_128x256, TILE_256x256, TILE_128x128, TILE_256x256_4W, TILE_256x256_4W_K64B, TILE_256x192 = (
+    0, 1, 2, 3, 4, 5, 6)
 SPT_OK, SPT_ERR_INVALID, SPT_ERR_UNSUPPORTED, SPT_ERR_MISALIGNED, SPT_ERR_LAUNCH = 0, -1, -2, -3, -4
 
 DTYPE_CODES = {"f16": F16, "bf16": BF16, "i8": I8, "f32": F32}

@@ -64,11 +64,14 @@ const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int s
 //    4000 x 3000 x 1000..4000, 3000^3, 5000^2 x 1024 and 8000 x 2000 x 8000
 //    run 4-25% faster on the 256 x 256 tile; 2000 x 4000 x 1000, 4100^3 and
 //    6000^2 x 2000, whose large tiles leave CUs idle or a long partial round,
-//    run faster on 128 x 256.
+//    run faster on 128 x 256.  Where the 8-wave 256 x 256 grid would leave CUs
+//    idle in its single round and a 256 x 192 grid still fits one round, the
+//    256 x 192 tile: 2-11% faster on 4000 x 3000 x 1000, 3000^3, 4000 x 3008 x
+//    4000, 2048 x 6144 x 2048 and 4096 x 3072 x 1024 (bit-identical results).
 // Variant: the DIRECT ring, 2 stages for 128-byte K tiles (two fill the LDS),
 // else 3.
 static constexpr int64_t kCus = 256;
-static void resolve(int dtype, int64_t M, int64_t N, int64_t K, int& variant, int& stages, int& tile)
+static void resolve(int dtype, int b_layout, int64_t M, int64_t N, int64_t K, int& variant, int& stages, int& tile)
 {
     if (variant == V_PERSIST && tile == 0) tile = 3;
     if (tile == 0) {
@@ -89,6 +92,12 @@ static void resolve(int dtype, int64_t M, int64_t N, int64_t K, int& variant, in
             // load2 <= (c1 / 2) / 0.9
             const bool big = mid && (deep || load2 == 1) && 9 * load2 <= 5 * c1;
             tile = big ? 2 : 1;
+            // A 256 x 256 grid that leaves CUs idle in its one round, where the
+            // 256 x 192 grid still fits one round: each CU then computes 3/4 as much,
+            // at ~1.25x the cost per FLOP (more copies and LDS reads per FLOP).
+            const int64_t n6 = ((M + 255) / 256) * ((N + 191) / 192);
+            // (not int8 with row-major B: its 192-byte k-rows take the slower lane layout)
+            if (big && n2 < kCus && n6 <= kCus && !(dtype == DT_I8 && b_layout == SPT_ROW)) tile = 6;
         }
     }
     if (variant == V_AUTO) variant = V_DIRECT;
@@ -124,7 +133,7 @@ static int make_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, i
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(SPT_ERR_UNSUPPORTED, "size above 2^31-1");
     if (dtype == DT_I8 && K > 131071)
         return fail(SPT_ERR_UNSUPPORTED, "int8 K=%lld exceeds 131071 (exact int32 sum)", (long long)K);
-    resolve(dtype, M, N, K, variant, stages, tile);
+    resolve(dtype, b_layout, M, N, K, variant, stages, tile);
     if (!valid_pair(variant, stages))
         return fail(SPT_ERR_UNSUPPORTED, "variant %d has no %d-stage form", variant, stages);
     if (variant == V_PERSIST && tile != 3)

@@ -25,6 +25,7 @@ constexpr TileShape kTiles[] = {
     {128, 128, 64, 2, 2},     // SPT_TILE_128x128, 256 threads
     {256, 256, 128, 2, 2},    // SPT_TILE_256x256_4W, 256 threads, 128 x 128 per wave
     {256, 256, 64, 2, 2},     // SPT_TILE_256x256_4W_K64B: the same with a 64-byte K depth
+    {256, 192, 128, 2, 4},    // SPT_TILE_256x192, 512 threads, 128 x 48 per wave
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 

@@ -79,11 +79,12 @@ constexpr KernelEntry pentry()
 #define SPT_TABLE_ENTRIES(DT, BC)                                                                      \
     SPT_RING_ONLY(DT, BC, 1), SPT_RING34(DT, BC, 1), SPT_EXACT34(DT, BC, 1), SPT_RING_ONLY(DT, BC, 2),   \
         entry<DT, BC, 3, V_DIRECT, 2>(), SPT_RING34(DT, BC, 3), SPT_RING_ONLY(DT, BC, 4),               \
-        SPT_RING_ONLY(DT, BC, 5), SPT_RING34(DT, BC, 5), SPT_EXACT34(DT, BC, 5), SPT_PERSIST(DT, BC)
+        SPT_RING_ONLY(DT, BC, 5), SPT_RING34(DT, BC, 5), SPT_EXACT34(DT, BC, 5), SPT_RING_ONLY(DT, BC, 6),  \
+        SPT_PERSIST(DT, BC)
 #else
 #define SPT_TABLE_ENTRIES(DT, BC)                                                                      \
     SPT_TILE_ALL(DT, BC, 1), SPT_TILE_BIG(DT, BC, 2), SPT_PAIRS(DT, BC, 3), SPT_RING34(DT, BC, 3),      \
-        SPT_TILE_BIG(DT, BC, 4), SPT_TILE_ALL(DT, BC, 5), SPT_PERSIST(DT, BC)
+        SPT_TILE_BIG(DT, BC, 4), SPT_TILE_ALL(DT, BC, 5), SPT_TILE_BIG(DT, BC, 6), SPT_PERSIST(DT, BC)
 #endif
 #define SPT_DEFINE_TABLE(NAME, DT, BC)                                                          \
     static const KernelEntry k_##NAME[] = {                                                    \

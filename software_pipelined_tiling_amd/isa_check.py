@@ -60,7 +60,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # Tile menu (BM, BN, K depth in bytes, waves along M, waves along N): the same
 # values as kTiles in csrc/spt_config.h, restated to compute expected counts.
 TILES = {1: (128, 256, 64, 2, 2), 2: (256, 256, 128, 2, 4), 3: (128, 128, 64, 2, 2),
-         4: (256, 256, 128, 2, 2), 5: (256, 256, 64, 2, 2)}
+         4: (256, 256, 128, 2, 2), 5: (256, 256, 64, 2, 2), 6: (256, 192, 128, 2, 4)}
 ELT = {0: 2, 1: 2, 2: 1, 3: 4}
 VARIANTS = {1: "sync", 2: "reg", 3: "direct"}
 _CFG = re.compile(r"CfgILi(\d+)ELb(\d)ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)ELb(\d)E")

@@ -63,7 +63,8 @@ def ex(M=64, N=64, K=64, A=PA, lda=None, B=PB, ldb=None, C=PC, ldc=None, dtype=s
     (dict(var=spt.VARIANT_SYNC, st=2), -2), (dict(var=spt.VARIANT_DIRECT, st=1), -2),
     (dict(var=spt.VARIANT_REG, st=3), -2), (dict(dtype=spt.I8, K=131072), -2),
     (dict(var=spt.VARIANT_DIRECT, st=3, tile=spt.TILE_256x256), -2),
-    (dict(var=spt.VARIANT_DIRECT, st=3, tile=spt.TILE_256x256_4W), -2), (dict(tile=6), -1),
+    (dict(var=spt.VARIANT_DIRECT, st=3, tile=spt.TILE_256x256_4W), -2), (dict(tile=7), -1),
+    (dict(var=spt.VARIANT_DIRECT, st=3, tile=spt.TILE_256x192), -2),
     (dict(var=spt.VARIANT_DIRECT, st=4, tile=spt.TILE_256x256), -2),
     (dict(A=0x8000), -2), (dict(B=1 << 47), -2),
     (dict(A=PA + 8), -3), (dict(B=PB + 2), -3), (dict(C=PC + 4), -3),
@@ -155,11 +156,14 @@ def test_pages_tile_plan(L):
     (spt.BF16, 8192, 8192, 512, spt.ROW, 1, 3),     # low K: the C store decides
     (spt.BF16, 8192, 8192, 64, spt.ROW, 1, 3),
     (spt.F16, 256, 256, 256, spt.ROW, 3, 3),        # too few 128 x 256 tiles for the CUs
-    (spt.BF16, 4000, 3000, 1000, spt.ROW, 2, 2),    # one round of 256 x 256 tiles
-    (spt.BF16, 3000, 3000, 3000, spt.ROW, 2, 2),
-    (spt.F16, 5000, 5000, 1024, spt.ROW, 2, 2),
-    (spt.F16, 8000, 2000, 8000, spt.ROW, 2, 2),
-    (spt.I8, 4000, 3008, 4000, spt.COL, 2, 2),
+    (spt.BF16, 4000, 3000, 1000, spt.ROW, 6, 2),    # 256 x 256 would leave CUs idle in its one
+    (spt.BF16, 3000, 3000, 3000, spt.ROW, 6, 2),    # round; 256 x 192 still fits one round
+    (spt.I8, 4000, 3008, 4000, spt.COL, 6, 2),
+    (spt.I8, 4000, 3008, 4000, spt.ROW, 2, 2),      # (int8 row-major B: 256 x 256 kept)
+    (spt.BF16, 2048, 6144, 2048, spt.ROW, 6, 2),
+    (spt.BF16, 4096, 3072, 1024, spt.ROW, 6, 2),
+    (spt.F16, 5000, 5000, 1024, spt.ROW, 2, 2),     # 256 x 256 tiles over more than one round
+    (spt.F16, 8000, 2000, 8000, spt.ROW, 2, 2),     # ... or exactly one round of all CUs
     (spt.BF16, 2000, 4000, 1000, spt.ROW, 1, 3),    # 256 x 256 would leave half the CUs idle
     (spt.F16, 4100, 4100, 4100, spt.ROW, 1, 3),     # ... or a long partial round
     (spt.F16, 6000, 6000, 2000, spt.ROW, 1, 3),

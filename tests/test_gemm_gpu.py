@@ -21,14 +21,15 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 PAIRS = [("sync", 1), ("reg", 1), ("reg", 2), ("direct", 2), ("direct", 3), ("direct", 4)]
-TILES = [1, 2, 3, 4, 5]
+TILES = [1, 2, 3, 4, 5, 6]
 SENT_F = np.uint32(0x7FC00ABC)   # a NaN payload no kernel produces
 SENT_I = np.int32(0x7FFFFFFF)
 
 
 def built(tile, variant, stages):
-    """Rings of 64 KiB stages (tiles 2 and 4) hold two stages at most in 160 KiB of LDS."""
-    return not (tile in (2, 4) and variant == "direct" and stages >= 3)
+    """Rings of 64 KiB and 56 KiB stages (tiles 2, 4 and 6) hold two stages at most in
+    160 KiB of LDS."""
+    return not (tile in (2, 4, 6) and variant == "direct" and stages >= 3)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -301,9 +302,10 @@ def test_full_fp16_4096(oracle_mod, variant, stages):
     sampled(oracle_mod, I.W_F16_4096, variant, stages, 1)
 
 
-@pytest.mark.parametrize("tile,stages", [(2, 2), (4, 2), (5, 2), (5, 3), (5, 4), (1, 4)])
+@pytest.mark.parametrize("tile,stages", [(2, 2), (4, 2), (5, 2), (5, 3), (5, 4), (1, 4), (6, 2)])
 def test_full_fp16_4096_ring_tiles(oracle_mod, tile, stages):
-    """The exact-fit ring kernels of the other tiles at the full 4096^3 size."""
+    """The ring kernels of the other tiles at the full 4096^3 size (exact-fit,
+    except the 256 x 192 tile, whose grid has a ragged last column)."""
     sampled(oracle_mod, I.W_F16_4096, "direct", stages, tile)
 
 
@@ -311,6 +313,27 @@ def test_full_fp16_4096_ring_tiles(oracle_mod, tile, stages):
                                                  ("direct", 2, 4), ("direct", 3, 5)])
 def test_full_int8_4096_bcol(oracle_mod, variant, stages, tile):
     sampled(oracle_mod, I.W_I8_4096, variant, stages, tile)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8", "f32"])
+@pytest.mark.parametrize("b_col", [False, True])
+@pytest.mark.parametrize("M,N,K", [(512, 768, 640), (256, 384, 128), (500, 700, 333)])
+def test_tile_256x192_all_pairs(oracle_mod, dtype, b_col, M, N, K):
+    """The 256 x 192 tile: shapes that are multiples of it (exact-fit kernels)
+    and a ragged one (general kernels); every (variant, stages) pair agrees
+    with the oracle and bit for bit with the others."""
+    K = K if dtype != "f32" else K // 2
+    A, B = operands(dtype, b_col, M, N, K, 13, lda_pad=0 if M % 256 == 0 else 8, ldb_pad=0 if M % 256 == 0 else 8)
+    Cref = ref(oracle_mod, A, B, dtype, b_col, N, K)
+    outs = []
+    for v, st in PAIRS:
+        if not built(6, v, st):
+            continue
+        C = run(A, B, dtype, b_col, M, N, K, v, st, 6)
+        parity.check_full(C, Cref, A, B, dtype, b_col, M, N, K)
+        outs.append(C)
+    for C in outs[1:]:
+        assert np.array_equal(C.view(np.uint32), outs[0].view(np.uint32)), (dtype, b_col, M, N, K)
 
 
 @pytest.mark.parametrize("dtype", ["f16", "i8"])
@@ -336,14 +359,18 @@ def test_full_bf16_lowk(oracle_mod, K):
     sampled(oracle_mod, I.w_bf16_lowk(K))
 
 
-@pytest.mark.parametrize("w", [I.Workload("bf16 GEMM 3000x3000x3000", 31, "bf16", 3000, 3000, 3000),
-                               I.Workload("int8 GEMM 4000x3008x4000, B column-major", 32, "i8", 4000, 3008, 4000,
-                                          True)], ids=["bf16_3000", "i8_4000x3008"])
-def test_full_auto_large_tile_shapes(oracle_mod, w):
-    """Shapes on which the library's choice is the 8-wave 256 x 256 tile (general
-    kernel: edges and a K tail): sampled outputs against the oracle, int8 bit-exact."""
+@pytest.mark.parametrize("w,tile", [
+    (I.Workload("bf16 GEMM 3000x3000x3000", 31, "bf16", 3000, 3000, 3000), 6),
+    (I.Workload("int8 GEMM 4000x3008x4000, B column-major", 32, "i8", 4000, 3008, 4000, True), 6),
+    (I.Workload("fp16 GEMM 8000x2000x8000", 33, "f16", 8000, 2000, 8000), 2)],
+    ids=["bf16_3000", "i8_4000x3008", "f16_8000x2000"])
+def test_full_auto_large_tile_shapes(oracle_mod, w, tile):
+    """Shapes on which the library's choice is an 8-wave tile: 256 x 192 where a
+    256 x 256 grid would leave CUs idle in its one round, 256 x 256 where it fills
+    them (general kernels: edges and a K tail): sampled outputs against the oracle,
+    int8 bit-exact."""
     rc, pi = spt.spt_plan(spt.DTYPE_CODES[w.dtype], w.M, w.N, w.K, spt.COL if w.b_col else spt.ROW)
-    assert rc == 0 and pi.tile_id == 2
+    assert rc == 0 and pi.tile_id == tile
     sampled(oracle_mod, w)
 
 

@@ -34,11 +34,11 @@ def pick(ks, **kw):
 
 
 def test_every_built_entry_is_in_the_binary(kernels):
-    # 8 tables (element type x B layout) of 46: SYNC, REG 1/2 and DIRECT 2 on every tile,
+    # 8 tables (element type x B layout) of 54: SYNC, REG 1/2 and DIRECT 2 on every tile,
     # DIRECT 3/4 where the ring fits in LDS (tiles 1, 3, 5), and exact-fit forms of all
-    # of these on tiles 1, 2, 4 and 5
-    assert len(kernels) == 8 * 46
-    assert {k.tile for k in kernels} == {1, 2, 3, 4, 5}
+    # of these on tiles 1, 2, 4, 5 and 6
+    assert len(kernels) == 8 * 54
+    assert {k.tile for k in kernels} == {1, 2, 3, 4, 5, 6}
 
 
 @pytest.mark.parametrize("dtype", [0, 1])
@@ -190,7 +190,7 @@ def test_checks_catch_planted_schedule_faults(kernels, tile, stages):
 
 # The kernels the library's own choice runs, and the exact-fit forms that the pipelining
 # comparisons time (every (variant, stages) pair of a tile in the same form as its ring).
-AUTO_CHOICES = {(1, "direct", 3), (2, "direct", 2), (3, "direct", 3), (4, "direct", 2)}
+AUTO_CHOICES = {(1, "direct", 3), (2, "direct", 2), (3, "direct", 3), (4, "direct", 2), (6, "direct", 2)}
 COMPARED = {("sync", 1), ("reg", 1), ("reg", 2), ("direct", 2)}
 
 
@@ -202,13 +202,13 @@ def test_default_and_compared_kernels_keep_scratch_out_of_the_loop(kernels):
     seen = 0
     for k in kernels:
         auto = (k.tile, k.variant, k.stages) in AUTO_CHOICES and (k.tile != 4 or k.exact)
-        compared = k.exact and k.tile in (1, 2, 4, 5) and (k.variant, k.stages) in COMPARED
+        compared = k.exact and k.tile in (1, 2, 4, 5, 6) and (k.variant, k.stages) in COMPARED
         if not (auto or compared):
             continue
         seen += 1
         assert X.loop_stats(k)["scratch"] == 0, k.name
         if not (k.dtype == 2 and not k.bcol and k.tile == 2 and not k.exact):
             assert k.meta["vgpr_spill"] == 0 and k.meta["scratch"] == 0, (k.name, k.meta)
-    # per table: 6 selectable (tiles 1 and 2 in both forms, 3 general, 4 exact) and 16 compared,
-    # 2 of them in both sets
-    assert seen == 8 * (6 + 16 - 2)
+    # per table: 8 selectable (tiles 1, 2 and 6 in both forms, 3 general, 4 exact) and 20
+    # compared, 3 of them in both sets
+    assert seen == 8 * (8 + 20 - 3)
