@@ -424,3 +424,40 @@ def test_extreme_aspect_ratios(oracle_mod, dtype, b_col, M, N, K):
     for v, s in (("auto", 0), ("sync", 1)):
         C = run(A, B, dtype, b_col, M, N, K, v, s)
         parity.check_full(C, Cref, A, B, dtype, b_col, M, N, K)
+
+
+def _random_shapes(n=32):
+    """Seeded shapes across element types and B layouts, large enough that AUTO picks
+    every tile family (128 x 128 up to the 256 x 256 and 256 x 192 tiles)."""
+    rng = np.random.default_rng(20261202)
+    out = []
+    for i in range(n):
+        dtype = ["f16", "bf16", "i8", "f32"][i % 4]
+        b_col = bool((i // 4) % 2)
+        M, N = (int(x) for x in rng.integers(1, 5200, 2))
+        K = int(rng.integers(1, 3000 if dtype != "f32" else 800))
+        out.append((dtype, b_col, M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("dtype,b_col,M,N,K", _random_shapes())
+def test_auto_random_shapes(oracle_mod, dtype, b_col, M, N, K):
+    """AUTO on seeded random shapes, pitches padded to 16-byte multiples: sampled
+    outputs against the oracle (int8 bit-exact), every output written and nothing
+    written outside M x N."""
+    rc, pi = spt.spt_plan(spt.DTYPE_CODES[dtype], M, N, K, spt.COL if b_col else spt.ROW)
+    assert rc == 0
+    print(f"[gpu] random {dtype} {'col' if b_col else 'row'} {M}x{N}x{K} tile {pi.tile_id}", flush=True)
+    A, B = operands(dtype, b_col, M, N, K, 40 + M % 50, pad_nan=False)
+    dA, dB = to_dev(A, dtype), to_dev(B, dtype)
+    ldc = -(-(N + 1) // 4) * 4  # a 16-byte pitch with at least one padding column
+    C = alloc_c(M, ldc, dtype)
+    launch(dA, dB, C, dtype, M, N, K, A.shape[1], B.shape[1], b_col)
+    sent = int(SENT_I) if dtype == "i8" else int(np.array(SENT_F).view(np.int32))
+    raw = C.view(torch.int32)
+    assert bool((raw[:, N:] == sent).all()), "write outside M x N"
+    assert not bool((raw[:, :N] == sent).any()), "output left unwritten"
+    rows, cols = parity.sample_entries(M, N, 600, np.random.default_rng(M * 7 + N))
+    got = C[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()].cpu().numpy()
+    want = oracle_mod.gemm_entries(A, B, dtype, rows, cols, b_col=b_col, K=K)
+    parity.check_entries(got, want, rows, cols, A, B, dtype, b_col, M, N, K)
