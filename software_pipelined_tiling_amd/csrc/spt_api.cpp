@@ -68,6 +68,11 @@ const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int s
 //    idle in its single round and a 256 x 192 grid still fits one round, the
 //    256 x 192 tile: 2-11% faster on 4000 x 3000 x 1000, 3000^3, 4000 x 3008 x
 //    4000, 2048 x 6144 x 2048 and 4096 x 3072 x 1024 (bit-identical results).
+//    Exact-fit fp16/bf16 shapes whose 256 x 256 grid ends in a partly filled
+//    round also take the 256 x 192 tile when 0.9 x its rounds are fewer:
+//    4608^3, 6144^3, 6144^2 x 2048 and 4096 x 6144 x 4096 run 9-13% faster;
+//    4096^3, 5120^2 x 4096, 5376^2 x 4096, 7168^2 x 4096 and 8192^3 keep
+//    256 x 256 (the 256 x 192 tile measured 2-35% slower there).
 // Variant: the DIRECT ring, 2 stages for 128-byte K tiles (two fill the LDS),
 // else 3.
 static constexpr int64_t kCus = 256;
@@ -83,6 +88,11 @@ static void resolve(int dtype, int b_layout, int64_t M, int64_t N, int64_t K, in
         const int64_t n2 = ((M + 255) / 256) * ((N + 255) / 256);
         if (fits4 && n4 >= kCus) {
             tile = 4;
+            // A partly filled last round of 256 x 256 tiles: the 256 x 192 grid when its
+            // rounds, at 3/4 of the work and ~1.2x the cost per FLOP, take less
+            // (fp16/bf16 with N a multiple of 192, as measured).
+            const int64_t n6e = (M / 256) * (N / 192);
+            if (elt == 2 && N % 192 == 0 && 9 * ((n6e + kCus - 1) / kCus) < 10 * ((n4 + kCus - 1) / kCus)) tile = 6;
         } else if (n1 < kCus) {
             tile = 3;
         } else {

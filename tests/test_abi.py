@@ -152,6 +152,13 @@ def test_pages_tile_plan(L):
 # ---- the library's choice (AUTO) ------------------------------------------------
 @pytest.mark.parametrize("dtype,M,N,K,lay,tile,stages", [
     (spt.F16, 4096, 4096, 4096, spt.ROW, 4, 2),     # exact 256 x 256, long K
+    (spt.F16, 8192, 8192, 8192, spt.ROW, 4, 2),
+    (spt.F16, 5120, 5120, 4096, spt.ROW, 4, 2),
+    (spt.F16, 7168, 7168, 4096, spt.ROW, 4, 2),
+    (spt.F16, 4608, 4608, 4608, spt.ROW, 6, 2),     # a partly filled last round of 256 x 256
+    (spt.F16, 6144, 6144, 6144, spt.ROW, 6, 2),
+    (spt.BF16, 6144, 6144, 2048, spt.ROW, 6, 2),
+    (spt.F16, 4096, 6144, 4096, spt.ROW, 6, 2),
     (spt.I8, 4096, 4096, 4096, spt.COL, 4, 2),
     (spt.BF16, 8192, 8192, 512, spt.ROW, 1, 3),     # low K: the C store decides
     (spt.BF16, 8192, 8192, 64, spt.ROW, 1, 3),
