@@ -106,11 +106,11 @@ DTYPES = [(spt.F16, 2), (spt.BF16, 2), (spt.I8, 1), (spt.F32, 4)]
 PAIRS = [(spt.VARIANT_SYNC, 1), (spt.VARIANT_REG, 1), (spt.VARIANT_REG, 2), (spt.VARIANT_DIRECT, 2),
          (spt.VARIANT_DIRECT, 3), (spt.VARIANT_DIRECT, 4)]
 TILES = {1: (128, 256, 64, 256), 2: (256, 256, 128, 512), 3: (128, 128, 64, 256), 4: (256, 256, 128, 256),
-         5: (256, 256, 64, 256)}
+         5: (256, 256, 64, 256), 6: (256, 192, 128, 512)}
 
 
 @pytest.mark.parametrize("dtype,elt", DTYPES)
-@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("tile", sorted(TILES))
 @pytest.mark.parametrize("var,st", PAIRS)
 def test_plan_matches_page_formulas(L, dtype, elt, tile, var, st):
     BM, BN, BKB, thr = TILES[tile]
