@@ -72,7 +72,9 @@ const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int s
 //    round also take the 256 x 192 tile when 0.9 x its rounds are fewer:
 //    4608^3, 6144^3, 6144^2 x 2048 and 4096 x 6144 x 4096 run 9-13% faster;
 //    4096^3, 5120^2 x 4096, 5376^2 x 4096, 7168^2 x 4096 and 8192^3 keep
-//    256 x 256 (the 256 x 192 tile measured 2-35% slower there).
+//    256 x 256 (the 256 x 192 tile measured 2-35% slower there).  int8 with
+//    column-major B follows the same rule: 13-18% faster on 4608^3, 6144^3 and
+//    4096 x 6144 x 4096, slower on 5120^2 x 4096 and 8192^3.
 // Variant: the DIRECT ring, 2 stages for 128-byte K tiles (two fill the LDS),
 // else 3.
 static constexpr int64_t kCus = 256;
@@ -90,9 +92,11 @@ static void resolve(int dtype, int b_layout, int64_t M, int64_t N, int64_t K, in
             tile = 4;
             // A partly filled last round of 256 x 256 tiles: the 256 x 192 grid when its
             // rounds, at 3/4 of the work and ~1.2x the cost per FLOP, take less
-            // (fp16/bf16 with N a multiple of 192, as measured).
+            // (fp16/bf16, and int8 with column-major B, N a multiple of 192: as measured).
             const int64_t n6e = (M / 256) * (N / 192);
-            if (elt == 2 && N % 192 == 0 && 9 * ((n6e + kCus - 1) / kCus) < 10 * ((n4 + kCus - 1) / kCus)) tile = 6;
+            const bool measured = elt == 2 || (dtype == DT_I8 && b_layout == SPT_COL);
+            if (measured && N % 192 == 0 && 9 * ((n6e + kCus - 1) / kCus) < 10 * ((n4 + kCus - 1) / kCus))
+                tile = 6;
         } else if (n1 < kCus) {
             tile = 3;
         } else {

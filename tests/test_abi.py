@@ -159,6 +159,9 @@ def test_pages_tile_plan(L):
     (spt.F16, 6144, 6144, 6144, spt.ROW, 6, 2),
     (spt.BF16, 6144, 6144, 2048, spt.ROW, 6, 2),
     (spt.F16, 4096, 6144, 4096, spt.ROW, 6, 2),
+    (spt.I8, 4608, 4608, 4608, spt.COL, 6, 2),
+    (spt.I8, 5120, 5120, 4096, spt.COL, 4, 2),
+    (spt.I8, 4608, 4608, 4608, spt.ROW, 4, 2),      # (int8 row-major B: 256 x 256 kept)
     (spt.I8, 4096, 4096, 4096, spt.COL, 4, 2),
     (spt.BF16, 8192, 8192, 512, spt.ROW, 1, 3),     # low K: the C store decides
     (spt.BF16, 8192, 8192, 64, spt.ROW, 1, 3),

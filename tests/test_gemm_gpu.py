@@ -363,8 +363,9 @@ def test_full_bf16_lowk(oracle_mod, K):
     (I.Workload("bf16 GEMM 3000x3000x3000", 31, "bf16", 3000, 3000, 3000), 6),
     (I.Workload("int8 GEMM 4000x3008x4000, B column-major", 32, "i8", 4000, 3008, 4000, True), 6),
     (I.Workload("fp16 GEMM 8000x2000x8000", 33, "f16", 8000, 2000, 8000), 2),
-    (I.Workload("fp16 GEMM 4608x4608x4608", 34, "f16", 4608, 4608, 4608), 6)],
-    ids=["bf16_3000", "i8_4000x3008", "f16_8000x2000", "f16_4608"])
+    (I.Workload("fp16 GEMM 4608x4608x4608", 34, "f16", 4608, 4608, 4608), 6),
+    (I.Workload("int8 GEMM 4608x4608x4608, B column-major", 35, "i8", 4608, 4608, 4608, True), 6)],
+    ids=["bf16_3000", "i8_4000x3008", "f16_8000x2000", "f16_4608", "i8_4608"])
 def test_full_auto_large_tile_shapes(oracle_mod, w, tile):
     """Shapes on which the library's choice is an 8-wave tile: 256 x 192 where a
     256 x 256 grid would leave CUs idle in its one round or end in a partly filled
