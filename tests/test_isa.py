@@ -212,3 +212,28 @@ def test_default_and_compared_kernels_keep_scratch_out_of_the_loop(kernels):
     # per table: 8 selectable (tiles 1, 2 and 6 in both forms, 3 general, 4 exact) and 20
     # compared, 3 of them in both sets
     assert seen == 8 * (8 + 20 - 3)
+
+
+def test_poison_build_writes_before_every_refill():
+    """In the race-detection library (libspt_poison.so), every ring kernel's steady
+    loop follows each barrier with one poison write per copy the wave will issue,
+    then lgkmcnt(0), and only then the copies that refill the stage.  (So a read
+    of that stage before its copies land meets the poison; see
+    tests/test_poison_gpu.py.)"""
+    from software_pipelined_tiling_amd import build as b
+    if not os.path.exists(b.POISON_LIB):
+        pytest.skip("libspt_poison.so not built")
+    ks = [k for k in X.load(b.POISON_LIB) if k.variant == "direct"]
+    assert len(ks) == 2 * 21  # the ring kernels of fp16 row-major B and int8 column-major B
+    for k in ks:
+        body = X.steady_loop(k)
+        loads = k.geometry["loads_per_tile"]
+        bars = [i for i, o in enumerate(body) if o.startswith("s_barrier")]
+        assert len(bars) == k.geometry["tiles_per_iter"], k.name
+        for b0 in bars:
+            first_copy = next(i for i in range(b0, len(body)) if body[i].startswith("buffer_load")
+                              and body[i].rstrip().endswith("lds"))
+            seg = body[b0:first_copy]
+            writes = [i for i, o in enumerate(seg) if o.startswith("ds_write")]
+            assert len(writes) == loads, (k.name, len(writes), loads)
+            assert any(o.startswith("s_waitcnt") and "lgkmcnt(0)" in o for o in seg[writes[-1]:]), k.name
