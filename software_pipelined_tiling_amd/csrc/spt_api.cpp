@@ -72,13 +72,14 @@ const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int s
 //    round also take the 256 x 192 tile when 0.9 x its rounds are fewer:
 //    4608^3, 6144^3, 6144^2 x 2048 and 4096 x 6144 x 4096 run 9-13% faster;
 //    4096^3, 5120^2 x 4096, 5376^2 x 4096, 7168^2 x 4096 and 8192^3 keep
-//    256 x 256 (the 256 x 192 tile measured 2-35% slower there).  int8 with
-//    column-major B follows the same rule: 13-18% faster on 4608^3, 6144^3 and
-//    4096 x 6144 x 4096, slower on 5120^2 x 4096 and 8192^3.
+//    256 x 256 (the 256 x 192 tile measured 2-35% slower there).  int8
+//    follows the same rule: with column-major B 13-18% faster on 4608^3, 6144^3
+//    and 4096 x 6144 x 4096, slower on 5120^2 x 4096 and 8192^3; with row-major
+//    B 20% faster than the 256 x 256 tile on 4608^3.
 // Variant: the DIRECT ring, 2 stages for 128-byte K tiles (two fill the LDS),
 // else 3.
 static constexpr int64_t kCus = 256;
-static void resolve(int dtype, int b_layout, int64_t M, int64_t N, int64_t K, int& variant, int& stages, int& tile)
+static void resolve(int dtype, int64_t M, int64_t N, int64_t K, int& variant, int& stages, int& tile)
 {
     if (variant == V_PERSIST && tile == 0) tile = 3;
     if (tile == 0) {
@@ -92,11 +93,9 @@ static void resolve(int dtype, int b_layout, int64_t M, int64_t N, int64_t K, in
             tile = 4;
             // A partly filled last round of 256 x 256 tiles: the 256 x 192 grid when its
             // rounds, at 3/4 of the work and ~1.2x the cost per FLOP, take less
-            // (fp16/bf16, and int8 with column-major B, N a multiple of 192: as measured).
+            // (fp16/bf16 and int8, N a multiple of 192: as measured).
             const int64_t n6e = (M / 256) * (N / 192);
-            const bool measured = elt == 2 || (dtype == DT_I8 && b_layout == SPT_COL);
-            if (measured && N % 192 == 0 && 9 * ((n6e + kCus - 1) / kCus) < 10 * ((n4 + kCus - 1) / kCus))
-                tile = 6;
+            if (elt <= 2 && N % 192 == 0 && 9 * ((n6e + kCus - 1) / kCus) < 10 * ((n4 + kCus - 1) / kCus)) tile = 6;
         } else if (n1 < kCus) {
             tile = 3;
         } else {
@@ -110,8 +109,7 @@ static void resolve(int dtype, int b_layout, int64_t M, int64_t N, int64_t K, in
             // 256 x 192 grid still fits one round: each CU then computes 3/4 as much,
             // at ~1.25x the cost per FLOP (more copies and LDS reads per FLOP).
             const int64_t n6 = ((M + 255) / 256) * ((N + 191) / 192);
-            // (not int8 with row-major B: its 192-byte k-rows take the slower lane layout)
-            if (big && n2 < kCus && n6 <= kCus && !(dtype == DT_I8 && b_layout == SPT_ROW)) tile = 6;
+            if (big && n2 < kCus && n6 <= kCus) tile = 6;
         }
     }
     if (variant == V_AUTO) variant = V_DIRECT;
@@ -147,7 +145,7 @@ static int make_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, i
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(SPT_ERR_UNSUPPORTED, "size above 2^31-1");
     if (dtype == DT_I8 && K > 131071)
         return fail(SPT_ERR_UNSUPPORTED, "int8 K=%lld exceeds 131071 (exact int32 sum)", (long long)K);
-    resolve(dtype, b_layout, M, N, K, variant, stages, tile);
+    resolve(dtype, M, N, K, variant, stages, tile);
     if (!valid_pair(variant, stages))
         return fail(SPT_ERR_UNSUPPORTED, "variant %d has no %d-stage form", variant, stages);
     if (variant == V_PERSIST && tile != 3)

@@ -116,10 +116,7 @@ struct Cfg {
     static constexpr int DT = DT_;
     static constexpr bool BCOL = BCOL_;
     static constexpr bool EXACT = EXACT_;
-    // (also when a k-row of B is not a whole number of 8-chunk groups, which the row
-    // layout's chunk swizzle permutes within: int8 rows of the 192-column tile)
-    static constexpr bool BLANE =
-        BLANE_ || elt_bytes(DT_) == 4 || (!BCOL_ && (kTiles[TILE_].BN * elt_bytes(DT_) / 16) % 8 != 0);
+    static constexpr bool BLANE = BLANE_ || elt_bytes(DT_) == 4;
     static constexpr int TILE = TILE_, V = V_, S = S_;
     static constexpr int BM = kTiles[TILE_].BM, BN = kTiles[TILE_].BN;
     static constexpr int ELT = elt_bytes(DT_);
@@ -257,8 +254,11 @@ struct Gemm {
     // Row-major B, row layout: k-rows of RN = BN * ELT bytes (NCN chunks), chunk
     // c of k-row r at c ^ swz_n(r); read by ds_read_b64_tr_b16 / tr_b8.
     static constexpr int RN = C::BN * C::ELT, NCN = RN / 16;
-    static __device__ __forceinline__ constexpr int swz_n(int r) { return C::ELT == 2 ? ((r & 3) << 1) : (r & 7); }
-    static_assert(C::BCOL || C::BLANE || NCN % 8 == 0, "the k-row swizzle permutes chunks within groups of 8");
+    // The XOR permutes chunks within groups of SWG: 8, or 4 for int8 k-rows of 12
+    // chunks (the 192-column tile), which hold no whole group of 8.
+    static constexpr int SWG = (C::ELT == 1 && NCN % 8 != 0) ? 4 : 8;
+    static __device__ __forceinline__ constexpr int swz_n(int r) { return C::ELT == 2 ? ((r & 3) << 1) : (r & (SWG - 1)); }
+    static_assert(C::BCOL || C::BLANE || NCN % SWG == 0, "the k-row swizzle permutes chunks within groups");
     // Row-major B, lane layout: block (nb, s, h) of 64 lanes x (8 | 8 | 4) bytes
     // in the order of the lanes of one ds_read_b64_tr_b16 / tr_b8 / ds_read_b32.
     static constexpr int BR_BLOCK = C::ELT == 4 ? 256 : 512;

@@ -161,7 +161,7 @@ def test_pages_tile_plan(L):
     (spt.F16, 4096, 6144, 4096, spt.ROW, 6, 2),
     (spt.I8, 4608, 4608, 4608, spt.COL, 6, 2),
     (spt.I8, 5120, 5120, 4096, spt.COL, 4, 2),
-    (spt.I8, 4608, 4608, 4608, spt.ROW, 4, 2),      # (int8 row-major B: 256 x 256 kept)
+    (spt.I8, 4608, 4608, 4608, spt.ROW, 6, 2),
     (spt.I8, 4096, 4096, 4096, spt.COL, 4, 2),
     (spt.BF16, 8192, 8192, 512, spt.ROW, 1, 3),     # low K: the C store decides
     (spt.BF16, 8192, 8192, 64, spt.ROW, 1, 3),
@@ -169,7 +169,6 @@ def test_pages_tile_plan(L):
     (spt.BF16, 4000, 3000, 1000, spt.ROW, 6, 2),    # 256 x 256 would leave CUs idle in its one
     (spt.BF16, 3000, 3000, 3000, spt.ROW, 6, 2),    # round; 256 x 192 still fits one round
     (spt.I8, 4000, 3008, 4000, spt.COL, 6, 2),
-    (spt.I8, 4000, 3008, 4000, spt.ROW, 2, 2),      # (int8 row-major B: 256 x 256 kept)
     (spt.BF16, 2048, 6144, 2048, spt.ROW, 6, 2),
     (spt.BF16, 4096, 3072, 1024, spt.ROW, 6, 2),
     (spt.F16, 5000, 5000, 1024, spt.ROW, 2, 2),     # 256 x 256 tiles over more than one round
