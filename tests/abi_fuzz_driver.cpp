@@ -139,7 +139,7 @@ int main()
     static const int64_t kPads[] = {0, 0, 0, 1, 8, 16, 64, -1};
     for (int it = 0; it < rounds; ++it) {
         const int dtype = (int)(next() % 4), layout = (int)(next() % 2), variant = (int)(next() % 5);
-        const int stages = (int)(next() % 5), tile = (int)(next() % 6);
+        const int stages = (int)(next() % 5), tile = (int)(next() % 7);
         const int64_t M = pick(kDims), N = pick(kDims), K = next() % 8 == 0 ? 0 : pick(kDims);
         const int64_t lda = K + pick(kPads), ldb = (layout ? K : N) + pick(kPads), ldc = N + pick(kPads);
         uintptr_t a = 0x7f0000000000ull, b = 0x7f4000000000ull, c = 0x7f8000000000ull;
