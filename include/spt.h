@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SPT_VERSION 10000 /* 1.0.0 = major*10000 + minor*100 + patch */
+#define SPT_VERSION 10100 /* 1.1.0 = major*10000 + minor*100 + patch */
 
 /* Element type of A and B (C is fp32, or int32 for SPT_I8). */
 enum spt_dtype { SPT_F16 = 0, SPT_BF16 = 1, SPT_I8 = 2, SPT_F32 = 3 };
@@ -181,6 +181,15 @@ typedef struct spt_plan_info {
                                        previous output tile (16 / store_window stores per K tile);
                                        else 0 */
     int32_t tiles_per_wg;           /* output tiles per workgroup: ceil(tiles_m * tiles_n / grid) */
+    /* Row band of a last, nearly empty round (AUTO choice only: tile, variant
+       and stages all 0; K of at least 2 KiB per row).  When band_tile > 0,
+       `grid` workgroups compute rows [0, band_m) of C as above, then, in stream
+       order, band_grid workgroups of the 128 x 128 tile (3-stage DIRECT ring)
+       compute rows [band_m, M): two launches.  Each output is the same sum in
+       the same order either way.  band_tile = 0: one launch, band_m = M. */
+    int32_t band_tile;
+    int64_t band_m;
+    int64_t band_grid;
 } spt_plan_info;
 
 /* C = A*B with B row-major, the library's choice of tile and variant. */

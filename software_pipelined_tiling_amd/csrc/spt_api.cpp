@@ -2,6 +2,7 @@
 // dispatch of the K-loop kernels (declared in include/spt.h).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -131,6 +132,38 @@ static bool valid_pair(int variant, int stages)
            ((variant == V_DIRECT || variant == V_PERSIST) && stages >= 2 && stages <= 4);
 }
 
+// Row band of a nearly empty last round.  A grid whose last round fills at
+// most half of the resident workgroup slots (two per CU where the LDS holds
+// two, else one) runs the whole rows of tiles that fit the earlier rounds,
+// then the rows below them (the band) as a second launch of 128 x 128 tiles
+// (3-stage DIRECT ring): twice the workgroups of 128 x 256 tiles, each with
+// half the work, so the band takes less of a round.  K of at least 2 KiB per
+// row: measured through AUTO (medians, us, one grid -> main + band) fp16
+// 4100 x 4104 x 4104 170.3 -> 169.1, int8 4100 x 4112 x 4112 (B col) 125.1 ->
+// 117.3, bf16 6000^2 x 2000 152.2 -> 149.4, fp32 4100^2 x 1024 348.7 -> 300.5,
+// int8 4224 x 4096 x 8192 170.8 -> 162.5, bf16 8448 x 8192 x 2048 257.8 -> 244.6,
+// fp16 4352 x 4096 x 8192 329.5 -> 257.7; below 2 KiB fp16 4224 x 4000 x 520
+// lost (41.2 -> 44.3).
+// (Splitting the band over K instead, added into C with device-scope atomics,
+// measured 1.3-2.2x slower than no split at all.)
+static constexpr int kBandTile = 3;
+static void plan_band(int64_t M, int64_t N, int64_t K, spt_plan_info& p)
+{
+    if (K * p.elt_bytes < 2048) return;
+    const int64_t per_cu = std::min<int64_t>(2, kLdsPerCu / p.lds_bytes);
+    const int64_t cap = kCus * per_cu, total = p.tiles_m * p.tiles_n;
+    if (total <= cap) return;
+    const int64_t rounds = (total + cap - 1) / cap, last = total - (rounds - 1) * cap;
+    if (2 * last > cap) return;
+    const int64_t rows_main = (rounds - 1) * cap / p.tiles_n;  // whole rows of tiles before the band
+    if (rows_main <= 0 || rows_main >= p.tiles_m) return;
+    const TileShape& T = kTiles[kBandTile];
+    p.band_tile = kBandTile;
+    p.band_m = rows_main * p.BM;
+    p.band_grid = ((M - p.band_m + T.BM - 1) / T.BM) * ((N + T.BN - 1) / T.BN);
+    p.grid = rows_main * p.tiles_n;
+}
+
 // Checks every argument except the pointers; fills `pi` on success.
 static int make_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, int variant,
                      int stages, int tile, spt_plan_info* pi)
@@ -145,6 +178,7 @@ static int make_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, i
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(SPT_ERR_UNSUPPORTED, "size above 2^31-1");
     if (dtype == DT_I8 && K > 131071)
         return fail(SPT_ERR_UNSUPPORTED, "int8 K=%lld exceeds 131071 (exact int32 sum)", (long long)K);
+    const bool auto_choice = variant == V_AUTO && stages == 0 && tile == 0;
     resolve(dtype, M, N, K, variant, stages, tile);
     if (!valid_pair(variant, stages))
         return fail(SPT_ERR_UNSUPPORTED, "variant %d has no %d-stage form", variant, stages);
@@ -183,7 +217,7 @@ static int make_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, i
         if (p.grid > resident) p.grid = resident;
         p.store_window = store_window(p.k_full_tiles);
     }
-    p.tiles_per_wg = p.grid > 0 ? (int32_t)((p.tiles_m * p.tiles_n + p.grid - 1) / p.grid) : 0;
+    p.band_m = M;
     p.k_tail = (int32_t)(K - p.k_full_tiles * p.BK);
     // "Pipeline GPU Kernel", Schritt 1: smem_a = BM*BK*sizeof(T), smem_b = BK*BN*sizeof(T).
     p.a_stage_bytes = p.BM * p.BK * elt;
@@ -204,6 +238,9 @@ static int make_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, i
         p.steady_vmcnt = (stages - 2) * (p.a_copies_per_thread + p.b_copies_per_thread) +
                          (stages - 1) * ((p.wave_m / 16) * (p.wave_n / 16) / p.store_window);
     // one 16x16 MFMA step covers 64 bytes of k per lane group; fp32 issues 4 MFMAs per step
+    if (auto_choice && variant == V_DIRECT) plan_band(M, N, K, p);
+    p.tiles_per_wg = p.grid > 0 ? (int32_t)((p.tiles_m * p.tiles_n + p.grid - 1) / p.grid) : 0;
+    if (p.band_tile) p.tiles_per_wg = 1;
     const int kstep = 4 * (16 / elt);
     p.mfma_per_ktile_per_wave = (p.wave_m / 16) * (p.wave_n / 16) * (p.BK / kstep) * (dtype == DT_F32 ? 4 : 1);
     // "Pipeline GPU Kernel", Schritt 2: 2*BM*BN*BK / ((BM*BK + BK*BN) * sizeof(T)).
@@ -263,8 +300,15 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     // (same arithmetic, no tail or edge code), else the general one.
     // A tile of one 64-byte MFMA k-step runs its ring in pairs of tiles (the
     // register slot of step 0 alternates); the exact-fit form has no odd last tile.
+    // Row band (AUTO): the band kernel's B panel must also fit 32-bit offsets,
+    // else the grid runs as one launch.
+    const TileShape& TB = kTiles[kBandTile];
+    bool band = pi.band_tile > 0;
+    if (band && (bcol ? (int64_t)TB.BN * ldb * elt : (int64_t)(TB.BKB / elt) * ldb * elt) >= lim) band = false;
+    const int64_t M_main = band ? pi.band_m : M;
+    const int64_t grid = band ? pi.grid : pi.tiles_m * pi.tiles_n;
     const bool one_step = kTiles[pi.tile_id].BKB == 64;
-    const bool fits = M % pi.BM == 0 && N % pi.BN == 0 && pi.k_tail == 0 && (!one_step || pi.k_full_tiles % 2 == 0);
+    const bool fits = M_main % pi.BM == 0 && N % pi.BN == 0 && pi.k_tail == 0 && (!one_step || pi.k_full_tiles % 2 == 0);
     const KernelEntry* e = nullptr;
     if (pi.variant == V_PERSIST) {
         if (!fits || pi.k_full_tiles < 2 || pi.store_window < pi.stages - 1)
@@ -281,23 +325,39 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     }
     if (!e) return fail(SPT_ERR_UNSUPPORTED, "no kernel built for dtype %d layout %d tile %d variant %d stages %d",
                         dtype, b_layout, pi.tile_id, pi.variant, pi.stages);
+    const KernelEntry* eb = band ? find_kernel(dtype, bcol, kBandTile, V_DIRECT, 3, 0) : nullptr;
+    if (band && !eb) return fail(SPT_ERR_UNSUPPORTED, "no band kernel built for dtype %d layout %d", dtype, b_layout);
 
     GemmArgs a;
     a.A = (const char*)A;
     a.B = (const char*)B;
     a.C = (char*)C;
-    a.M = (int)M;
+    a.M = (int)M_main;
     a.N = (int)N;
     a.K = (int)K;
     a.lda = (int)lda;
     a.ldb = (int)ldb;
     a.ldc = (int)ldc;
-    a.tiles_m = (int)pi.tiles_m;
+    a.tiles_m = (int)(band ? M_main / pi.BM : pi.tiles_m);
     a.tiles_n = (int)pi.tiles_n;
     a.k_full = (int)pi.k_full_tiles;
     a.k_tail = pi.k_tail;
-    const hipError_t err = e->launch(a, (unsigned)pi.grid, (hipStream_t)stream);
+    hipError_t err = e->launch(a, (unsigned)grid, (hipStream_t)stream);
     if (err != hipSuccess) return fail(SPT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(err));
+    if (band) {  // rows [M_main, M) on the band tile, after the main grid in stream order
+        GemmArgs b = a;
+        b.A = (const char*)A + M_main * lda * elt;
+        b.C = (char*)C + M_main * ldc * 4;
+        b.M = (int)(M - M_main);
+        b.tiles_m = (b.M + TB.BM - 1) / TB.BM;
+        b.tiles_n = (int)((N + TB.BN - 1) / TB.BN);
+        b.k_full = (int)(K / (TB.BKB / elt));
+        b.k_tail = (int)(K - (int64_t)b.k_full * (TB.BKB / elt));
+        if ((int64_t)b.tiles_m * b.tiles_n != pi.band_grid)
+            return fail(SPT_ERR_LAUNCH, "internal: band grid mismatch");
+        err = eb->launch(b, (unsigned)pi.band_grid, (hipStream_t)stream);
+        if (err != hipSuccess) return fail(SPT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(err));
+    }
     return SPT_OK;
 }
 

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert spt.spt_version() == 10000
+    assert spt.spt_version() == 10100
     assert spt.spt_status_string(0) == "SPT_OK"
     assert spt.spt_status_string(-1) == "SPT_ERR_INVALID"
     assert spt.spt_status_string(-2) == "SPT_ERR_UNSUPPORTED"
@@ -272,3 +272,38 @@ def test_last_error_describes_the_most_recent_call():
     assert spt.spt_scale_by_two(-1, 0, 0) == spt.SPT_ERR_INVALID
     assert spt.spt_scale_by_two(0, 0, 0) == spt.SPT_OK
     assert spt.spt_last_error() == ""
+
+
+@pytest.mark.parametrize("dtype,M,N,K,b_col,band_m", [
+    ("f16", 4100, 4104, 4104, False, 3840),
+    ("i8", 4100, 4112, 4112, True, 3840),
+    ("bf16", 6000, 6000, 2000, False, 5376),
+    ("f32", 4100, 4100, 1024, False, 3840),
+    ("bf16", 8448, 8192, 2048, False, 8192),  # 256 x 256 main grid
+    ("f16", 4352, 4096, 8192, False, 4096),
+    ("f16", 4224, 4000, 520, False, None),    # K below 2 KiB per row
+    ("f16", 4096, 4096, 4096, False, None),   # full rounds
+    ("f16", 5120, 5120, 4096, False, None),   # last round more than half full
+    ("bf16", 4000, 3000, 1000, False, None),  # one round
+])
+def test_row_band_plan(dtype, M, N, K, b_col, band_m):
+    """A last round at most half full: the rows of tiles that fit the earlier
+    rounds run as one grid, the rows below them as a second grid of 128 x 128
+    tiles."""
+    rc, pi = spt.spt_plan(spt.DTYPE_CODES[dtype], M, N, K, spt.COL if b_col else spt.ROW)
+    assert rc == 0
+    if band_m is None:
+        assert (pi.band_tile, pi.band_m, pi.band_grid) == (0, M, 0)
+        assert pi.grid == pi.tiles_m * pi.tiles_n
+        return
+    cap = 256 * min(2, 163840 // pi.lds_bytes)
+    assert (pi.band_tile, pi.band_m) == (spt.TILE_128x128, band_m)
+    total = pi.tiles_m * pi.tiles_n
+    rounds = -(-total // cap)
+    assert 2 * (total - (rounds - 1) * cap) <= cap           # last round at most half full
+    assert band_m % pi.BM == 0 and pi.grid == band_m // pi.BM * pi.tiles_n
+    assert (rounds - 1) * cap - pi.tiles_n < pi.grid <= (rounds - 1) * cap  # as many whole rows as fit
+    assert pi.band_grid == -(-(M - band_m) // 128) * -(-N // 128)
+    # explicit requests never split
+    rc, pe = spt.spt_plan(spt.DTYPE_CODES[dtype], M, N, K, spt.COL if b_col else spt.ROW, spt.VARIANT_DIRECT, 3, 1)
+    assert rc == 0 and pe.band_tile == 0 and pe.grid == pe.tiles_m * pe.tiles_n

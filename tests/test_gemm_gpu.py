@@ -376,6 +376,38 @@ def test_full_auto_large_tile_shapes(oracle_mod, w, tile):
     sampled(oracle_mod, w)
 
 
+# ---- row band of a nearly empty last round (AUTO) ----------------------------
+@pytest.mark.parametrize("dtype,b_col,K", [("f16", False, 1040), ("bf16", True, 1032), ("i8", True, 2100),
+                                           ("i8", False, 2100), ("f32", False, 524)])
+def test_row_band_full(oracle_mod, dtype, b_col, K):
+    """4224 x 4000: 33 x 16 tiles of 128 x 256, one more row of tiles than two
+    rounds of 512 hold; the last 128 rows run as a second grid of 128 x 128
+    tiles.  Every output against the oracle (int8 bit-exact), nothing written
+    past N, and bit-identical to the one-grid 128 x 256 kernel."""
+    M, N = 4224, 4000
+    rc, pi = spt.spt_plan(spt.DTYPE_CODES[dtype], M, N, K, spt.COL if b_col else spt.ROW)
+    assert rc == 0 and pi.band_tile == spt.TILE_128x128 and pi.band_m == 4096
+    A, B = operands(dtype, b_col, M, N, K, 40)
+    C = run(A, B, dtype, b_col, M, N, K)
+    parity.check_full(C, ref(oracle_mod, A, B, dtype, b_col, N, K), A, B, dtype, b_col, M, N, K)
+    C1 = run(A, B, dtype, b_col, M, N, K, "direct", 3, 1)
+    assert np.array_equal(C.view(np.uint32), C1.view(np.uint32))
+
+
+@pytest.mark.parametrize("w", [I.Workload("fp16 GEMM 4100x4104x4104", 41, "f16", 4100, 4104, 4104),
+                               I.Workload("int8 GEMM 4100x4112x4112, B column-major", 42, "i8", 4100, 4112, 4112,
+                                          True),
+                               I.Workload("fp16 GEMM 4352x4096x8192", 43, "f16", 4352, 4096, 8192)],
+                         ids=["f16_4100", "i8_4100", "f16_4352"])
+def test_full_row_band(oracle_mod, w):
+    """Full-size shapes whose last rows the library runs as a band of 128 x 128
+    tiles (after a 128 x 256 or a 256 x 256 grid): sampled outputs against the
+    oracle."""
+    rc, pi = spt.spt_plan(spt.DTYPE_CODES[w.dtype], w.M, w.N, w.K, spt.COL if w.b_col else spt.ROW)
+    assert rc == 0 and pi.band_tile == spt.TILE_128x128
+    sampled(oracle_mod, w)
+
+
 @pytest.mark.parametrize("variant,stages", [("auto", 0), ("reg", 2), ("sync", 1)])
 def test_full_bf16_ragged(oracle_mod, variant, stages):
     sampled(oracle_mod, I.W_BF16_RAGGED, variant, stages)
