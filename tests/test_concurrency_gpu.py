@@ -2,8 +2,9 @@
 
 Between calls the library keeps only a thread-local error message, so calls
 from several host threads, each on its own stream, must each give the C of a
-single call.  A call is one kernel launch with no allocation, copy or memset,
-so it can also be captured into a HIP graph: every replay must give the C of
+single call.  A call is one kernel launch (two where a last, nearly empty
+round runs as a second grid) with no allocation, copy or memset, so it can
+also be captured into a HIP graph: every replay must give the C of
 an eager call on the operands the buffers hold at that moment.
 """
 from __future__ import annotations
@@ -79,12 +80,16 @@ def test_errors_stay_with_their_thread():
     assert "dtype 9" in spt.spt_last_error()
 
 
-@pytest.mark.parametrize("dtype,b_col", [("f16", False), ("i8", True)])
-def test_captured_in_a_hip_graph(oracle_mod, dtype, b_col):
+@pytest.mark.parametrize("dtype,b_col,M,N,K", [("f16", False, 256, 384, 512), ("i8", True, 256, 384, 512),
+                                               ("f16", False, 4224, 4000, 1040)],
+                         ids=["f16", "i8_col", "f16_two_grids"])
+def test_captured_in_a_hip_graph(oracle_mod, dtype, b_col, M, N, K):
     """One call captured into a graph, replayed six times over two operand sets
     that eager copies swap in between replays (C reset to a sentinel each time):
-    every replay bit-identical to the eager call on the same operands."""
-    M, N, K = 256, 384, 512
+    every replay bit-identical to the eager call on the same operands.  The
+    4224 x 4000 call is two launches (a grid, then a band of 128 x 128 tiles)."""
+    rc, pi = spt.spt_plan(spt.DTYPE_CODES[dtype], M, N, K, spt.COL if b_col else spt.ROW)
+    assert rc == 0 and (pi.band_tile > 0) == (M == 4224)
     sets = [operands(dtype, b_col, M, N, K, 71 + i, pad_nan=False) for i in range(2)]
     eager = [run(A, B, dtype, b_col, M, N, K, ldc_pad=0) for A, B in sets]
     for (A, B), C in zip(sets, eager):
