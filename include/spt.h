@@ -41,9 +41,11 @@
  * The library never allocates or frees device memory and keeps no pointer
  * after a call returns.  `stream` is a hipStream_t (NULL = the null
  * stream) of the calling thread's current HIP device, which must also hold
- * the matrices; the launch is asynchronous and the call never synchronizes.
- * SPT_ERR_LAUNCH carries the status of this call's own launch, not an error
- * left over from earlier HIP calls.
+ * the matrices.  A GEMM is one kernel launch, or two in stream order where
+ * spt_plan reports a row band (band_tile > 0); launches are asynchronous and
+ * the call never synchronizes.  SPT_ERR_LAUNCH carries the status of this
+ * call's own launches, not an error left over from earlier HIP calls (if the
+ * band's launch fails, C holds only rows [0, band_m)).
  * The library keeps no mutable global state apart from a thread-local
  * message for spt_last_error(); concurrent calls from several threads are
  * safe.
