@@ -142,8 +142,9 @@ static bool valid_pair(int variant, int stages)
 // 4100 x 4104 x 4104 170.3 -> 169.1, int8 4100 x 4112 x 4112 (B col) 125.1 ->
 // 117.3, bf16 6000^2 x 2000 152.2 -> 149.4, fp32 4100^2 x 1024 348.7 -> 300.5,
 // int8 4224 x 4096 x 8192 170.8 -> 162.5, bf16 8448 x 8192 x 2048 257.8 -> 244.6,
-// fp16 4352 x 4096 x 8192 329.5 -> 257.7; below 2 KiB fp16 4224 x 4000 x 520
-// lost (41.2 -> 44.3).
+// fp16 4352 x 4096 x 8192 329.5 -> 257.7, fp16 4608 x 5120 x 4096 (a band of
+// 480 workgroups) 190.4 -> 180.5, fp16 1152 x 32760 x 4096 366.2 -> 330.7;
+// below 2 KiB fp16 4224 x 4000 x 520 lost (41.2 -> 44.3).
 // (Splitting the band over K instead, added into C with device-scope atomics,
 // measured 1.3-2.2x slower than no split at all.)
 static constexpr int kBandTile = 3;
@@ -157,10 +158,16 @@ static void plan_band(int64_t M, int64_t N, int64_t K, spt_plan_info& p)
     if (2 * last > cap) return;
     const int64_t rows_main = (rounds - 1) * cap / p.tiles_n;  // whole rows of tiles before the band
     if (rows_main <= 0 || rows_main >= p.tiles_m) return;
+    // whole rows must nearly fill the earlier rounds (wide rows of tiles may
+    // not), and the band must fit one round of two 128 x 128 workgroups per CU
+    if ((rounds - 1) * cap - rows_main * p.tiles_n > cap / 8) return;
     const TileShape& T = kTiles[kBandTile];
+    const int64_t band_m = rows_main * p.BM;
+    const int64_t band_grid = ((M - band_m + T.BM - 1) / T.BM) * ((N + T.BN - 1) / T.BN);
+    if (band_grid > 2 * kCus) return;
     p.band_tile = kBandTile;
-    p.band_m = rows_main * p.BM;
-    p.band_grid = ((M - p.band_m + T.BM - 1) / T.BM) * ((N + T.BN - 1) / T.BN);
+    p.band_m = band_m;
+    p.band_grid = band_grid;
     p.grid = rows_main * p.tiles_n;
 }
 

@@ -285,6 +285,8 @@ def test_last_error_describes_the_most_recent_call():
     ("f16", 4096, 4096, 4096, False, None),   # full rounds
     ("f16", 5120, 5120, 4096, False, None),   # last round more than half full
     ("bf16", 4000, 3000, 1000, False, None),  # one round
+    ("f16", 512, 102408, 4096, False, None),  # rows of 401 tiles leave the main grid a partial round
+    ("f16", 4864, 5120, 4096, False, None),   # a band of 560 workgroups of 128 x 128
 ])
 def test_row_band_plan(dtype, M, N, K, b_col, band_m):
     """A last round at most half full: the rows of tiles that fit the earlier
@@ -303,6 +305,7 @@ def test_row_band_plan(dtype, M, N, K, b_col, band_m):
     assert 2 * (total - (rounds - 1) * cap) <= cap           # last round at most half full
     assert band_m % pi.BM == 0 and pi.grid == band_m // pi.BM * pi.tiles_n
     assert (rounds - 1) * cap - pi.tiles_n < pi.grid <= (rounds - 1) * cap  # as many whole rows as fit
+    assert (rounds - 1) * cap - pi.grid <= cap // 8 and pi.band_grid <= 512
     assert pi.band_grid == -(-(M - band_m) // 128) * -(-N // 128)
     # explicit requests never split
     rc, pe = spt.spt_plan(spt.DTYPE_CODES[dtype], M, N, K, spt.COL if b_col else spt.ROW, spt.VARIANT_DIRECT, 3, 1)
