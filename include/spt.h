@@ -186,10 +186,13 @@ typedef struct spt_plan_info {
     /* Row band of a last, nearly empty round (AUTO choice only: tile, variant
        and stages all 0; K of at least 2 KiB per row).  When band_tile > 0,
        `grid` workgroups compute rows [0, band_m) of C as above, then, in stream
-       order, band_grid workgroups of the 128 x 128 tile (3-stage DIRECT ring)
-       compute rows [band_m, M): two launches.  Each output is the same sum in
+       order, band_grid workgroups of the 128 x 128 tile (DIRECT ring of
+       band_stages stages: 4 for at most 256 workgroups and K of at least
+       8 KiB per row, else 3) compute rows
+       [band_m, M): two launches.  Each output is the same sum in
        the same order either way.  band_tile = 0: one launch, band_m = M. */
     int32_t band_tile;
+    int32_t band_stages;
     int64_t band_m;
     int64_t band_grid;
 } spt_plan_info;

@@ -54,7 +54,7 @@ class PlanInfo(ctypes.Structure):
         ("steady_vmcnt", ctypes.c_int32), ("mfma_per_ktile_per_wave", ctypes.c_int32),
         ("ratio_flop_per_byte", ctypes.c_double), ("ratio_mfma_per_load", ctypes.c_double),
         ("store_window", ctypes.c_int32), ("tiles_per_wg", ctypes.c_int32),
-        ("band_tile", ctypes.c_int32), ("band_m", ctypes.c_int64), ("band_grid", ctypes.c_int64),
+        ("band_tile", ctypes.c_int32), ("band_stages", ctypes.c_int32), ("band_m", ctypes.c_int64), ("band_grid", ctypes.c_int64),
     ]
 
     def as_dict(self) -> dict:

@@ -136,7 +136,7 @@ static bool valid_pair(int variant, int stages)
 // most half of the resident workgroup slots (two per CU where the LDS holds
 // two, else one) runs the whole rows of tiles that fit the earlier rounds,
 // then the rows below them (the band) as a second launch of 128 x 128 tiles
-// (3-stage DIRECT ring): twice the workgroups of 128 x 256 tiles, each with
+// (DIRECT ring): twice the workgroups of 128 x 256 tiles, each with
 // half the work, so the band takes less of a round.  K of at least 2 KiB per
 // row: measured through AUTO (medians, us, one grid -> main + band) fp16
 // 4100 x 4104 x 4104 170.3 -> 169.1, int8 4100 x 4112 x 4112 (B col) 125.1 ->
@@ -166,6 +166,13 @@ static void plan_band(int64_t M, int64_t N, int64_t K, spt_plan_info& p)
     const int64_t band_grid = ((M - band_m + T.BM - 1) / T.BM) * ((N + T.BN - 1) / T.BN);
     if (band_grid > 2 * kCus) return;
     p.band_tile = kBandTile;
+    // a band of at most one workgroup per CU with K of at least 8 KiB per row
+    // hides more latency with 4 stages (fp16 band rows alone, us, 3 -> 4
+    // stages: 256 x 4096 x 8192 68.8 -> 60.1, 128 x 32760 x 4096 66.1 -> 63.4,
+    // 260 x 4104 x 4104 42.9 -> 42.8); a band of two per CU keeps 3 (1536 x 5120
+    // x 4096: 76.5 against 77.0), and so does bf16 6000^2 x 2000 (AUTO 149.4 us
+    // with 3 stages, 157.5 with 4)
+    p.band_stages = band_grid <= kCus && K * p.elt_bytes >= 8192 ? 4 : 3;
     p.band_m = band_m;
     p.band_grid = band_grid;
     p.grid = rows_main * p.tiles_n;
@@ -332,7 +339,7 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     }
     if (!e) return fail(SPT_ERR_UNSUPPORTED, "no kernel built for dtype %d layout %d tile %d variant %d stages %d",
                         dtype, b_layout, pi.tile_id, pi.variant, pi.stages);
-    const KernelEntry* eb = band ? find_kernel(dtype, bcol, kBandTile, V_DIRECT, 3, 0) : nullptr;
+    const KernelEntry* eb = band ? find_kernel(dtype, bcol, kBandTile, V_DIRECT, pi.band_stages, 0) : nullptr;
     if (band && !eb) return fail(SPT_ERR_UNSUPPORTED, "no band kernel built for dtype %d layout %d", dtype, b_layout);
 
     GemmArgs a;

@@ -295,7 +295,7 @@ def test_row_band_plan(dtype, M, N, K, b_col, band_m):
     rc, pi = spt.spt_plan(spt.DTYPE_CODES[dtype], M, N, K, spt.COL if b_col else spt.ROW)
     assert rc == 0
     if band_m is None:
-        assert (pi.band_tile, pi.band_m, pi.band_grid) == (0, M, 0)
+        assert (pi.band_tile, pi.band_stages, pi.band_m, pi.band_grid) == (0, 0, M, 0)
         assert pi.grid == pi.tiles_m * pi.tiles_n
         return
     cap = 256 * min(2, 163840 // pi.lds_bytes)
@@ -306,6 +306,7 @@ def test_row_band_plan(dtype, M, N, K, b_col, band_m):
     assert band_m % pi.BM == 0 and pi.grid == band_m // pi.BM * pi.tiles_n
     assert (rounds - 1) * cap - pi.tiles_n < pi.grid <= (rounds - 1) * cap  # as many whole rows as fit
     assert (rounds - 1) * cap - pi.grid <= cap // 8 and pi.band_grid <= 512
+    assert pi.band_stages == (4 if pi.band_grid <= 256 and K * pi.elt_bytes >= 8192 else 3)
     assert pi.band_grid == -(-(M - band_m) // 128) * -(-N // 128)
     # explicit requests never split
     rc, pe = spt.spt_plan(spt.DTYPE_CODES[dtype], M, N, K, spt.COL if b_col else spt.ROW, spt.VARIANT_DIRECT, 3, 1)
