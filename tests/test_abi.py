@@ -311,3 +311,26 @@ def test_row_band_plan(dtype, M, N, K, b_col, band_m):
     # explicit requests never split
     rc, pe = spt.spt_plan(spt.DTYPE_CODES[dtype], M, N, K, spt.COL if b_col else spt.ROW, spt.VARIANT_DIRECT, 3, 1)
     assert rc == 0 and pe.band_tile == 0 and pe.grid == pe.tiles_m * pe.tiles_n
+
+
+def test_plan_info_mirror_matches_the_c_layout(tmp_path):
+    """The ctypes mirror of spt_plan_info has the C struct's size and every
+    field at the C offset (gcc on include/spt.h)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not installed")
+    fields = [f for f, _ in spt.PlanInfo._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "spt.h"\nint main(void) {\n'
+                   '    printf("size %zu\\n", sizeof(spt_plan_info));\n'
+                   + "".join(f'    printf("{f} %zu\\n", offsetof(spt_plan_info, {f}));\n' for f in fields)
+                   + "    return 0;\n}\n")
+    exe = tmp_path / "layout"
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(root, "include"), "-o", str(exe), str(src)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                      check=True).stdout.splitlines())
+    assert int(got["size"]) == ctypes.sizeof(spt.PlanInfo)
+    for f in fields:
+        assert int(got[f]) == getattr(spt.PlanInfo, f).offset, f
