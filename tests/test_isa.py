@@ -190,7 +190,8 @@ def test_checks_catch_planted_schedule_faults(kernels, tile, stages):
 
 # The kernels the library's own choice runs, and the exact-fit forms that the pipelining
 # comparisons time (every (variant, stages) pair of a tile in the same form as its ring).
-AUTO_CHOICES = {(1, "direct", 3), (2, "direct", 2), (3, "direct", 3), (4, "direct", 2), (6, "direct", 2)}
+AUTO_CHOICES = {(1, "direct", 3), (2, "direct", 2), (3, "direct", 3), (3, "direct", 4), (4, "direct", 2),
+                (6, "direct", 2)}
 COMPARED = {("sync", 1), ("reg", 1), ("reg", 2), ("direct", 2)}
 
 
@@ -209,9 +210,9 @@ def test_default_and_compared_kernels_keep_scratch_out_of_the_loop(kernels):
         assert X.loop_stats(k)["scratch"] == 0, k.name
         if not (k.dtype == 2 and not k.bcol and k.tile == 2 and not k.exact):
             assert k.meta["vgpr_spill"] == 0 and k.meta["scratch"] == 0, (k.name, k.meta)
-    # per table: 8 selectable (tiles 1, 2 and 6 in both forms, 3 general, 4 exact) and 20
-    # compared, 3 of them in both sets
-    assert seen == 8 * (8 + 20 - 3)
+    # per table: 9 selectable (tiles 1, 2 and 6 in both forms, 3 general with 3 and 4 stages
+    # (4: a row band), 4 exact) and 20 compared, 3 of them in both sets
+    assert seen == 8 * (9 + 20 - 3)
 
 
 def test_poison_build_writes_before_every_refill():
