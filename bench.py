@@ -23,7 +23,8 @@ Besides the headline value it reports, in the same line:
                 headline kernel runs back to back for a few seconds, and the
                 dense peak at that clock (context for the roofline fraction)
   mfma_ceiling  the rate MFMAs alone sustain with the headline's operand data
-                under the power limit (spt_probe_mfma), and value / that rate
+                under the power limit (spt_probe_mfma in libspt_probe.so, built from
+                bench_probe.hip), and value / that rate
   vendor_hipblaslt  the vendor library (torch.mm with fp32 output, torch._int_mm
                 for int8) on the same operands, per workload too (context only)
 """
@@ -170,6 +171,44 @@ def time_calls(prob: Problem, steps: int, warmup: int, variant="auto", stages=0,
     return e0.elapsed_time(e1) / steps
 
 
+def preheat(prob: Problem, seconds: float, variant="auto", stages=0, tile=0):
+    """Run the call back to back, untimed, for `seconds` of wall time, so that the
+    timed region starts with the GPU past its idle state and its clock settled
+    under the power limit (a fresh GPU ramps for tens of ms).  Returns the calls made."""
+    import torch
+    import software_pipelined_tiling_amd as spt
+    a = prob.args(torch.cuda.current_stream().cuda_stream, variant, stages, tile)
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(100):
+            spt.spt_gemm_ex(*a)
+        torch.cuda.synchronize()
+        n += 100
+    return n
+
+
+def time_calls_each(prob: Problem, steps: int, warmup: int, variant="auto", stages=0, tile=0):
+    """`steps` back-to-back calls with a HIP event recorded on the launch stream
+    before the first call and after every call: (mean ms per call over the whole
+    region, list of per-call microseconds)."""
+    import torch
+    import software_pipelined_tiling_amd as spt
+    stream = torch.cuda.current_stream()
+    a = prob.args(stream.cuda_stream, variant, stages, tile)
+    for _ in range(warmup):
+        spt.spt_gemm_ex(*a)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(steps):
+        spt.spt_gemm_ex(*a)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)]
+    return ev[0].elapsed_time(ev[steps]) / steps, per
+
+
 def cpu_baseline(w, budget_s: float):
     """The CPU oracle (as it stands) on the first rows of the same workload."""
     from oracle import oracle as O
@@ -186,8 +225,20 @@ def cpu_baseline(w, budget_s: float):
     dt = time.perf_counter() - t0
     flops = 2.0 * rows * w.N * w.K
     return {"value": round(flops / dt / 1e9, 2), "unit": "GFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"rows 0..{rows - 1} of C ({rows} x {w.N} outputs, full K={w.K}) of {w.name}; "
                       f"{dt:.1f} s on {cores} threads"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def traffic_from_profile(kernel_sha: str):
@@ -251,6 +302,26 @@ def stream_bench(steps: int, warmup: int):
     return out
 
 
+_probe = None
+
+
+def probe_lib():
+    """libspt_probe.so (bench_probe.hip): the sustained-MFMA probe, a measurement
+    tool kept out of libspt.so."""
+    global _probe
+    if _probe is None:
+        import ctypes
+        from software_pipelined_tiling_amd import build as B
+        if not os.path.exists(B.PROBE_LIB):
+            raise RuntimeError(f"{B.PROBE_LIB} not built (software_pipelined_tiling_amd.build.build_probe)")
+        L = ctypes.CDLL(B.PROBE_LIB)
+        L.spt_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+        L.spt_probe_mfma.restype = ctypes.c_int
+        _probe = L
+    return _probe
+
+
 def mfma_ceiling(prob: "Problem", seconds: float):
     """Sustained rate of MFMAs alone (spt_probe_mfma, no memory traffic in the
     loop) with the headline's own A matrix as operand data: the compute roof
@@ -264,7 +335,8 @@ def mfma_ceiling(prob: "Problem", seconds: float):
     code = spt.DTYPE_CODES[prob.w.dtype]
 
     def launch():
-        return spt.spt_probe_mfma(code, prob.dA.data_ptr(), nbytes, iters, sink.data_ptr(), stream.cuda_stream)
+        return probe_lib().spt_probe_mfma(code, prob.dA.data_ptr(), nbytes, iters, sink.data_ptr(),
+                                          stream.cuda_stream)
     if launch() != 0:
         return None
     for _ in range(100):
@@ -360,6 +432,9 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=300,
                     help="untimed calls first; the GPU's clock settles within ~30 ms of load")
+    ap.add_argument("--preheat", type=float, default=1.0,
+                    help="seconds of untimed back-to-back headline calls before the warm-up (a fresh GPU "
+                         "leaves its idle clocks over tens of ms; disclosed in the output)")
     ap.add_argument("--tile", type=int, default=0, help="headline tile (0 = library default)")
     ap.add_argument("--variant", default="auto", help="headline variant (auto/sync/reg/direct/persist)")
     ap.add_argument("--stages", type=int, default=0, help="headline stages (0 = variant default)")
@@ -391,11 +466,18 @@ def main():
 
     head = Problem(I.W_F16_4096)
     w = head.w
-    # --- timed region: K back-to-back steps, synchronised on both sides ---
-    ms = time_calls(head, args.steps, args.warmup, args.variant, args.stages, args.tile)
-    if ms is None:
+    hv, hs, ht = args.variant, args.stages, args.tile
+    if time_calls(head, 1, 0, hv, hs, ht) is None:
         print(f"bench.py: headline configuration refused: {spt.spt_last_error()}", file=sys.stderr)
         sys.exit(1)
+    # untimed pre-heat (disclosed in the line), then W warm-up calls, then the timed region:
+    # K back-to-back steps with a HIP event before the first and after every call
+    t_pre = time.perf_counter()
+    pre_calls = preheat(head, args.preheat, hv, hs, ht)
+    t_pre = time.perf_counter() - t_pre
+    ms, per_call = time_calls_each(head, args.steps, args.warmup, hv, hs, ht)
+    # the same region again with events around it only (do per-call events perturb it?)
+    ms_bracket = time_calls(head, args.steps, args.warmup, hv, hs, ht)
     tflops = w.flops / (ms * 1e-3) / 1e12
     rc, plan = spt.spt_plan(spt.F16, w.M, w.N, w.K, spt.ROW, spt.VARIANT_CODES[args.variant],
                             args.stages, args.tile)
@@ -414,6 +496,13 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
+        "timed_region": {"before": f"{pre_calls} untimed calls of the headline kernel back to back "
+                                   f"({t_pre:.2f} s pre-heat), then {args.warmup} warm-up calls",
+                         "per_call_us": [round(x, 2) for x in per_call] if len(per_call) <= 100 else None,
+                         "per_call_us_min_median_max": [round(min(per_call), 2),
+                                                        round(sorted(per_call)[len(per_call) // 2], 2),
+                                                        round(max(per_call), 2)],
+                         "repeat_events_around_region_only_ms": round(ms_bracket, 5)},
         "config": {"workload": w.name + ", A/B row-major, fp32 accumulate, fp32 C, U[-1,1] fp16",
                    "tile": f"{plan.BM}x{plan.BN}x{plan.BK}", "threads": plan.threads,
                    "variant": {1: "sync", 2: "reg", 3: "direct", 4: "persist"}[plan.variant],
@@ -495,6 +584,17 @@ def main():
                               "unpipelined_us": round(t1 * 1e3, 2),
                               "speedup_vs_unpipelined": round(t1 / t, 3)}
             extra[wk.name]["vendor_hipblaslt_us"] = vendor_us(p, steps)
+            if wk is I.W_F16_256:
+                # the small case: the single-stage loop beside the 2-stage (and deeper) pipelines,
+                # on the tile the library picks and on the pages' 128 x 256 x 32 tile
+                rc, pp = spt.spt_plan(spt.F16, wk.M, wk.N, wk.K, spt.ROW)
+                for tile in sorted({pp.tile_id, 1}):
+                    row = {}
+                    for v, s_ in PAIRS:
+                        tv = time_calls(p, max(steps, 200), 100, v, s_, tile)
+                        if tv is not None:
+                            row[f"{v}{s_}"] = round(tv * 1e3, 2)
+                    extra[wk.name][f"variants_us_tile{tile}"] = row
             if wk.K <= 1024 and wk.M * wk.N >= 1 << 24:
                 # the C store alone: the same kernel with K = 0 (it writes zeros to all of C)
                 extra[wk.name]["c_store_only_us"] = c_store_only(p, steps)

@@ -15,7 +15,7 @@ import os
 
 __all__ = [
     "spt_gemm", "spt_gemm_ex", "spt_plan", "spt_status_string", "spt_last_error", "spt_version",
-    "spt_scale_by_two", "spt_probe_mfma", "gemm", "plan", "scale_by_two", "SptError", "PlanInfo", "lib_path",
+    "spt_scale_by_two", "gemm", "plan", "scale_by_two", "SptError", "PlanInfo", "lib_path",
     "F16", "BF16", "I8", "F32", "ROW", "COL", "VARIANT_AUTO", "VARIANT_SYNC", "VARIANT_REG",
     "VARIANT_DIRECT", "VARIANT_PERSIST", "TILE_AUTO", "TILE_128x256", "TILE_256x256", "TILE_128x128", "TILE_256x256_4W",
     "TILE_256x256_4W_K64B", "TILE_256x192",
@@ -92,8 +92,6 @@ def _load():
         L.spt_version.restype = i32
         L.spt_scale_by_two.argtypes = [i64, vp, vp, i32, i32, vp]
         L.spt_scale_by_two.restype = i32
-        L.spt_probe_mfma.argtypes = [i32, vp, i64, i64, vp, vp]
-        L.spt_probe_mfma.restype = i32
         _lib = L
     return _lib
 
@@ -124,10 +122,6 @@ def spt_plan(dtype, M, N, K, b_layout=ROW, variant=VARIANT_AUTO, stages=0, tile_
 
 def spt_scale_by_two(n, x, y, stages=0, blocks=0, stream=0) -> int:
     return _load().spt_scale_by_two(n, x, y, stages, blocks, stream)
-
-
-def spt_probe_mfma(dtype, operands, operand_bytes, iters, sink, stream=0) -> int:
-    return _load().spt_probe_mfma(dtype, operands, operand_bytes, iters, sink, stream)
 
 
 def spt_status_string(status: int) -> str:

@@ -19,7 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = [f"spt_kernels_{dt}_{lay}.hip" for dt in ("f16", "bf16", "i8", "f32") for lay in ("row", "col")]
-SOURCES += ["spt_stream.hip", "spt_probe.hip", "spt_api.cpp"]
+SOURCES += ["spt_stream.hip", "spt_api.cpp"]
 HEADERS = ["spt_kernel.hpp", "spt_persist.hpp", "spt_instances.hpp", "spt_registry.h", "spt_config.h"]
 
 # Packed-fp32 VALU instructions are disabled for all device code (-packed-fp32-ops).
@@ -38,9 +38,11 @@ def _compile(src: str, defines=(), tag: str = "") -> str:
 
 
 def build_all(verbose: bool = True) -> None:
-    """libspt.so and the race-detection libspt_poison.so, compiled side by side."""
-    with cf.ThreadPoolExecutor(max_workers=2) as ex:
-        for f in [ex.submit(build, verbose=verbose), ex.submit(build_poison, verbose=verbose)]:
+    """libspt.so, the race-detection libspt_poison.so and bench.py's measurement
+    probe libspt_probe.so, compiled side by side."""
+    with cf.ThreadPoolExecutor(max_workers=3) as ex:
+        for f in [ex.submit(build, verbose=verbose), ex.submit(build_poison, verbose=verbose),
+                  ex.submit(build_probe, verbose=verbose)]:
             f.result()
 
 
@@ -92,7 +94,7 @@ def build_poison(verbose: bool = True) -> str:
         f.write('#include "spt_registry.h"\nnamespace spt {\n')
         f.writelines(f"KernelTable kernels_{t}() {{ return KernelTable{{nullptr, 0}}; }}\n" for t in empty)
         f.write("}\n")
-    srcs = [f"spt_kernels_{t}.hip" for t in POISON_TABLES] + ["spt_stream.hip", "spt_probe.hip", "spt_api.cpp"]
+    srcs = [f"spt_kernels_{t}.hip" for t in POISON_TABLES] + ["spt_stream.hip", "spt_api.cpp"]
     with cf.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
         objs = list(ex.map(lambda s: _compile(s, ("SPT_POISON",), "_poison"), srcs))
     stub_obj = os.path.join(BUILD, "spt_poison_stub.o")
@@ -108,6 +110,24 @@ def build_poison(verbose: bool = True) -> str:
     if verbose:
         print(f"built {POISON_LIB}", file=sys.stderr)
     return POISON_LIB
+
+
+PROBE_SRC = os.path.join(ROOT, "bench_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libspt_probe.so")
+
+
+def build_probe(verbose: bool = True) -> str:
+    """``libspt_probe.so``: the sustained-MFMA probe that bench.py loads (a
+    measurement tool, not part of libspt.so or its C ABI)."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "-I", ROOT, "-shared", "-o", tmp, PROBE_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the probe:\n{r.stderr[-4000:]}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}", file=sys.stderr)
+    return PROBE_LIB
 
 
 def asm(src: str = "spt_kernels_f16_row.hip", out: str | None = None) -> str:

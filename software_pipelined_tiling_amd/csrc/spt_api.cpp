@@ -9,7 +9,6 @@
 #include <cstring>
 
 #include "../../include/spt.h"
-#include "../../include/spt_probe.h"
 #include "spt_config.h"
 #include "spt_registry.h"
 
@@ -80,6 +79,7 @@ const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int s
 // Variant: the DIRECT ring, 2 stages for 128-byte K tiles (two fill the LDS),
 // else 3.
 static constexpr int64_t kCus = 256;
+static constexpr int64_t kPersistResident = kCus * 2;  // two 128 x 128 workgroups per CU
 static void resolve(int dtype, int64_t M, int64_t N, int64_t K, int& variant, int& stages, int& tile)
 {
     if (variant == V_PERSIST && tile == 0) tile = 3;
@@ -227,8 +227,7 @@ static int make_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, i
         // The grid stays a multiple of the 8 XCDs, so that a workgroup's tile
         // stream stays on one XCD.  The previous tile's C is written over the
         // store window.
-        const int64_t resident = kCus * 2;
-        if (p.grid > resident) p.grid = resident;
+        if (p.grid > kPersistResident) p.grid = kPersistResident;
         p.store_window = store_window(p.k_full_tiles);
     }
     p.band_m = M;
@@ -264,6 +263,16 @@ static int make_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, i
         (double)p.mfma_per_ktile_per_wave / (double)(p.a_copies_per_thread + p.b_copies_per_thread);
     *pi = p;
     return SPT_OK;
+}
+
+// Workgroups of the main launch: one per output tile, except for the
+// persistent variant (at most the resident workgroups, each walking a stream
+// of tiles) and a row band (the whole rows of tiles before the band; the band
+// is a second launch).  spt_plan reports the same number.
+static int64_t main_grid(const spt_plan_info& pi, bool band)
+{
+    if (pi.variant == V_PERSIST || band) return pi.grid;
+    return pi.tiles_m * pi.tiles_n;
 }
 
 static int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
@@ -320,7 +329,9 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     bool band = pi.band_tile > 0;
     if (band && (bcol ? (int64_t)TB.BN * ldb * elt : (int64_t)(TB.BKB / elt) * ldb * elt) >= lim) band = false;
     const int64_t M_main = band ? pi.band_m : M;
-    const int64_t grid = band ? pi.grid : pi.tiles_m * pi.tiles_n;
+    const int64_t grid = main_grid(pi, band);
+    if (pi.variant == V_PERSIST && grid > kPersistResident)
+        return fail(SPT_ERR_LAUNCH, "internal: persistent grid of %lld workgroups", (long long)grid);
     const bool one_step = kTiles[pi.tile_id].BKB == 64;
     const bool fits = M_main % pi.BM == 0 && N % pi.BN == 0 && pi.k_tail == 0 && (!one_step || pi.k_full_tiles % 2 == 0);
     const KernelEntry* e = nullptr;
@@ -403,18 +414,6 @@ static int scale_by_two_impl(int64_t n, const void* x, void* y, int stages, int 
     return SPT_OK;
 }
 
-static int mfma_probe_impl(int dtype, const void* ops, int64_t bytes, int64_t iters, void* sink, void* stream)
-{
-    if (dtype != DT_F16 && dtype != DT_BF16 && dtype != DT_I8)
-        return fail(SPT_ERR_INVALID, "dtype %d: the probe covers f16, bf16 and i8", dtype);
-    if (!ops || !sink) return fail(SPT_ERR_INVALID, "operands or sink is null");
-    if (bytes < 16 || iters < 0) return fail(SPT_ERR_INVALID, "fewer than 16 operand bytes or negative iters");
-    if ((uintptr_t)ops % 16) return fail(SPT_ERR_MISALIGNED, "operands not 16-byte aligned");
-    const hipError_t err = launch_mfma_probe(dtype, ops, bytes / 16, iters, (float*)sink, (hipStream_t)stream);
-    if (err != hipSuccess) return fail(SPT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(err));
-    return SPT_OK;
-}
-
 // Every entry point returns through here: the thread's message describes its
 // most recent call, and is empty when that call succeeded.
 static int done(int status)
@@ -426,12 +425,6 @@ static int done(int status)
 }  // namespace spt
 
 extern "C" {
-
-int spt_probe_mfma(int dtype, const void* operands, int64_t operand_bytes, int64_t iters, void* sink, void* stream)
-{
-    return spt::done(spt::mfma_probe_impl(dtype, operands, operand_bytes, iters, sink, stream));
-}
-
 
 int spt_scale_by_two(int64_t n, const void* x, void* y, int stages, int blocks, void* stream)
 {

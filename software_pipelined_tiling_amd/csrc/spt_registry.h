@@ -36,10 +36,6 @@ KernelTable kernels_f32_col();
 // The streaming pipeline y = 2 x (spt_stream.hip); arguments already validated.
 hipError_t launch_scale_by_two(const void* x, void* y, int64_t n, int stages, unsigned blocks, hipStream_t stream);
 
-// The sustained-MFMA measurement probe (spt_probe.hip); arguments already validated.
-hipError_t launch_mfma_probe(int dtype, const void* ops, int64_t n_vec, int64_t iters, float* sink,
-                             hipStream_t stream);
-
 // nullptr when that combination is not built.  exact = 1 asks for the
 // instantiation that assumes M, N, K are multiples of the tile.
 const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int stages, int exact, int window = 0);

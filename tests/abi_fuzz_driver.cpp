@@ -23,7 +23,6 @@
 #include <hip/hip_runtime.h>
 
 #include "../include/spt.h"
-#include "../include/spt_probe.h"
 #include "../software_pipelined_tiling_amd/csrc/spt_registry.h"
 
 namespace spt {
@@ -38,7 +37,6 @@ SPT_EMPTY_TABLE(i8_col)
 SPT_EMPTY_TABLE(f32_row)
 SPT_EMPTY_TABLE(f32_col)
 hipError_t launch_scale_by_two(const void*, void*, int64_t, int, unsigned, hipStream_t) { return hipErrorInvalidValue; }
-hipError_t launch_mfma_probe(int, const void*, int64_t, int64_t, float*, hipStream_t) { return hipErrorInvalidValue; }
 }  // namespace spt
 
 static uint64_t state = 0x9E3779B97F4A7C15ull;
@@ -123,10 +121,6 @@ int main()
         rc = spt_scale_by_two(M, A, C, stages, variant, nullptr);
         expect(known(rc), "spt_scale_by_two status", rc);
         expect(rc != SPT_OK || M == 0, "OK with work to launch", rc);
-        message_ok(rc);
-
-        rc = spt_probe_mfma(dtype, A, K, N, C, nullptr);
-        expect(known(rc), "spt_probe_mfma status", rc);
         message_ok(rc);
 
         expect(spt_status_string(rc) != nullptr && spt_status_string(layout) != nullptr, "status string", rc);

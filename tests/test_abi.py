@@ -28,7 +28,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert names == sorted(["spt_gemm", "spt_gemm_ex", "spt_plan", "spt_status_string",
-                            "spt_last_error", "spt_version", "spt_scale_by_two", "spt_probe_mfma"])
+                            "spt_last_error", "spt_version", "spt_scale_by_two"])
     for n in names:
         assert hasattr(L, n), n
 
@@ -239,15 +239,6 @@ def test_scale_by_two_validation(L, kw, status):
 
 def test_scale_by_two_empty_is_ok(L):
     assert spt.spt_scale_by_two(0, 0, 0, 0, 0, 0) == 0
-
-
-@pytest.mark.parametrize("args,status", [
-    ((3, X0, 1024, 1, Y0), -1), ((0, 0, 1024, 1, Y0), -1), ((0, X0, 1024, 1, 0), -1), ((0, X0, 8, 1, Y0), -1),
-    ((0, X0, 1024, -1, Y0), -1), ((0, X0 + 4, 1024, 1, Y0), -3),
-])
-def test_probe_validation(L, args, status):
-    assert spt.spt_probe_mfma(*args, 0) == status
-    assert spt.spt_last_error() != ""
 
 
 def test_panel_above_2gib_is_refused(L):
