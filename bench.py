@@ -92,10 +92,11 @@ class Problem:
                 spt.COL if w.b_col else spt.ROW, spt.VARIANT_CODES[variant], stages, tile)
 
 
-def vendor_us(prob: Problem, steps: int):
+def vendor_us(prob: Problem, steps: int = 20):
     """Microseconds per call of the vendor library (hipBLASLt through torch) on the same
     device operands and the same output type: torch.mm(..., out_dtype=float32) for
-    fp16/bf16, torch._int_mm for int8.  Context only; None where torch has no such call."""
+    fp16/bf16, torch._int_mm for int8, timed like the library (time_graph).  Context
+    only; None where torch has no such call."""
     import torch
     w = prob.w
     a = prob.dA[:, :w.K]
@@ -107,47 +108,24 @@ def vendor_us(prob: Problem, steps: int):
     else:
         return None
     try:
-        fn()
-        for _ in range(20):
+        for _ in range(3):
             fn()
-        stream = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return round(e0.elapsed_time(e1) / steps * 1e3, 2)
-    except Exception:  # shape or type torch does not support
+        us = time_graph(lambda stream: fn() is not None, calls=steps)
+        return None if us is None else round(us, 2)
+    except Exception:  # shape or type torch does not support, or not capturable
         return None
 
 
-def c_store_only(prob: Problem, steps: int):
+def c_store_only(prob: Problem):
     """Microseconds per call of the plan the library picks for `prob`, run with K = 0:
     the kernel then only writes C (zeros), the floor under the C store of that plan."""
-    import torch
     import software_pipelined_tiling_amd as spt
     w = prob.w
     rc, pi = spt.spt_plan(spt.DTYPE_CODES[w.dtype], w.M, w.N, w.K, spt.COL if w.b_col else spt.ROW)
     if rc != 0:
         return None
-    stream = torch.cuda.current_stream()
-    a = (w.M, w.N, 0, prob.dA.data_ptr(), prob.A.shape[1], prob.dB.data_ptr(), prob.B.shape[1],
-         prob.C.data_ptr(), w.N, spt.DTYPE_CODES[w.dtype], stream.cuda_stream, spt.COL if w.b_col else spt.ROW,
-         pi.variant, pi.stages, pi.tile_id)
-    if spt.spt_gemm_ex(*a) != 0:
-        return None
-    for _ in range(20):
-        spt.spt_gemm_ex(*a)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(steps):
-        spt.spt_gemm_ex(*a)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return round(e0.elapsed_time(e1) / steps * 1e3, 2)
+    vname = {1: "sync", 2: "reg", 3: "direct", 4: "persist"}[pi.variant]
+    return gemm_us(prob, vname, pi.stages, pi.tile_id, K=0)
 
 
 def time_calls(prob: Problem, steps: int, warmup: int, variant="auto", stages=0, tile=0):
@@ -169,6 +147,49 @@ def time_calls(prob: Problem, steps: int, warmup: int, variant="auto", stages=0,
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def time_graph(fn, calls: int = 20, reps: int = 10):
+    """Microseconds per call of `fn(stream_handle)` with `calls` calls captured in one
+    HIP graph and the graph replayed `reps` times between two events (after one
+    untimed replay): the GPU time of back-to-back calls, host launch cost excluded
+    (short kernels launched one by one from Python would wait on the host)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        if fn(side.cuda_stream) is False:  # eager check (and warm-up) before capture
+            return None
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(calls):
+                fn(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / (reps * calls) * 1e3
+
+
+def gemm_us(prob: Problem, variant="auto", stages=0, tile=0, K=None):
+    """time_graph of one spt_gemm_ex configuration (None when the library refuses it)."""
+    import software_pipelined_tiling_amd as spt
+
+    def fn(stream):
+        a = list(prob.args(stream, variant, stages, tile))
+        if K is not None:
+            a[2] = K
+        return spt.spt_gemm_ex(*a) == 0
+    us = time_graph(fn)
+    return None if us is None else round(us, 2)
 
 
 def preheat(prob: Problem, seconds: float, variant="auto", stages=0, tile=0):
@@ -475,9 +496,10 @@ def main():
     t_pre = time.perf_counter()
     pre_calls = preheat(head, args.preheat, hv, hs, ht)
     t_pre = time.perf_counter() - t_pre
-    ms, per_call = time_calls_each(head, args.steps, args.warmup, hv, hs, ht)
-    # the same region again with events around it only (do per-call events perturb it?)
-    ms_bracket = time_calls(head, args.steps, args.warmup, hv, hs, ht)
+    ms = time_calls(head, args.steps, args.warmup, hv, hs, ht)
+    # a second pass of K calls with an event after every call: the per-call spread (the
+    # event records add a gap of a few us between kernels, so this pass runs slower)
+    ms_each, per_call = time_calls_each(head, args.steps, 0, hv, hs, ht)
     tflops = w.flops / (ms * 1e-3) / 1e12
     rc, plan = spt.spt_plan(spt.F16, w.M, w.N, w.K, spt.ROW, spt.VARIANT_CODES[args.variant],
                             args.stages, args.tile)
@@ -498,11 +520,16 @@ def main():
         "data": "synthetic",
         "timed_region": {"before": f"{pre_calls} untimed calls of the headline kernel back to back "
                                    f"({t_pre:.2f} s pre-heat), then {args.warmup} warm-up calls",
-                         "per_call_us": [round(x, 2) for x in per_call] if len(per_call) <= 100 else None,
-                         "per_call_us_min_median_max": [round(min(per_call), 2),
-                                                        round(sorted(per_call)[len(per_call) // 2], 2),
-                                                        round(max(per_call), 2)],
-                         "repeat_events_around_region_only_ms": round(ms_bracket, 5)},
+                         "events": "one HIP event before the first and one after the last timed call, "
+                                   "on the launch stream, synchronised on both sides",
+                         "per_call_pass": {
+                             "what": f"{args.steps} more calls right after the timed region with an event after "
+                                     "every call (the records add a gap between kernels)",
+                             "ms_per_call": round(ms_each, 5),
+                             "per_call_us": [round(x, 2) for x in per_call] if len(per_call) <= 100 else None,
+                             "per_call_us_min_median_max": [round(min(per_call), 2),
+                                                            round(sorted(per_call)[len(per_call) // 2], 2),
+                                                            round(max(per_call), 2)]}},
         "config": {"workload": w.name + ", A/B row-major, fp32 accumulate, fp32 C, U[-1,1] fp16",
                    "tile": f"{plan.BM}x{plan.BN}x{plan.BK}", "threads": plan.threads,
                    "variant": {1: "sync", 2: "reg", 3: "direct", 4: "persist"}[plan.variant],
@@ -534,7 +561,7 @@ def main():
                                            "sustained 2 s each"}
 
     if not args.only_headline:
-        vu = vendor_us(head, 50)
+        vu = vendor_us(head)
         if vu:
             out["vendor_hipblaslt"] = {"us": vu, "tflops": round(w.flops / (vu * 1e-6) / 1e12, 1),
                                        "value_over_vendor": round(vu / (ms * 1e3), 3),
@@ -573,17 +600,14 @@ def main():
             if args.only_workload and not wk.name.startswith(args.only_workload):
                 continue
             p = Problem(wk)
-            t = time_calls(p, steps, 100)
-            t1 = time_calls(p, steps, 100, "sync", 1)
+            us, us1 = gemm_us(p), gemm_us(p, "sync", 1)
             peak = PEAK_TFLOPS[wk.dtype]
-            tf = wk.flops / (t * 1e-3) / 1e12
-            extra[wk.name] = {"us": round(t * 1e3, 2), "tflops": round(tf, 1),
-                              "pct_of_peak": round(100 * tf / peak, 1),
-                              "hbm_gbs_alg": round(wk.alg_bytes / (t * 1e-3) / 1e9, 1),
-                              "pct_of_hbm": round(100 * wk.alg_bytes / (t * 1e-3) / 1e9 / HBM_GBS, 1),
-                              "unpipelined_us": round(t1 * 1e3, 2),
-                              "speedup_vs_unpipelined": round(t1 / t, 3)}
-            extra[wk.name]["vendor_hipblaslt_us"] = vendor_us(p, steps)
+            tf = wk.flops / (us * 1e-6) / 1e12
+            gbs = wk.alg_bytes / (us * 1e-6) / 1e9
+            extra[wk.name] = {"us": us, "tflops": round(tf, 1), "pct_of_peak": round(100 * tf / peak, 1),
+                              "hbm_gbs_alg": round(gbs, 1), "pct_of_hbm": round(100 * gbs / HBM_GBS, 1),
+                              "unpipelined_us": us1, "speedup_vs_unpipelined": round(us1 / us, 3)}
+            extra[wk.name]["vendor_hipblaslt_us"] = vendor_us(p)
             if wk is I.W_F16_256:
                 # the small case: the single-stage loop beside the 2-stage (and deeper) pipelines,
                 # on the tile the library picks and on the pages' 128 x 256 x 32 tile
@@ -591,13 +615,13 @@ def main():
                 for tile in sorted({pp.tile_id, 1}):
                     row = {}
                     for v, s_ in PAIRS:
-                        tv = time_calls(p, max(steps, 200), 100, v, s_, tile)
+                        tv = gemm_us(p, v, s_, tile)
                         if tv is not None:
-                            row[f"{v}{s_}"] = round(tv * 1e3, 2)
+                            row[f"{v}{s_}"] = tv
                     extra[wk.name][f"variants_us_tile{tile}"] = row
             if wk.K <= 1024 and wk.M * wk.N >= 1 << 24:
                 # the C store alone: the same kernel with K = 0 (it writes zeros to all of C)
-                extra[wk.name]["c_store_only_us"] = c_store_only(p, steps)
+                extra[wk.name]["c_store_only_us"] = c_store_only(p)
             if wk is I.W_I8_4096 and not args.no_power:  # the int8 compute roof for this data
                 ceil = mfma_ceiling(p, 2.0)
                 if ceil:
@@ -605,6 +629,8 @@ def main():
                     extra[wk.name]["value_over_ceiling"] = round(tf / ceil, 4)
             del p
         out["workloads"] = extra
+        out["workloads_timing"] = ("every side workload: 20 calls captured in one HIP graph, replayed 10 times "
+                                   "between two events after one untimed replay (GPU time of back-to-back calls)")
 
         if not args.only_workload:
             out["streaming"] = stream_bench(steps, 20)

@@ -256,3 +256,105 @@ int oracle_scale_by_two(int64_t n, const uint32_t* x, uint32_t* y)
     }
     return 0;
 }
+
+/*
+ * The attention-style consumer, the pages' high-ratio example.  "Kernel-
+ * Engpass analysieren" counts the work of flash attention as
+ * 4 * batch * heads * seq_len^2 * head_dim FLOP (Schritt 1: the two products
+ * of every query row with every key row, then every probability with every
+ * value row) and uses it as the kernel with many matrix instructions per tile
+ * load (Schritt 4 and the pitfalls).  Flash attention computes softmax
+ * attention; written out plainly for each of BH independent (batch, head)
+ * slices:
+ *
+ *        S[i][j] = scale * sum_{d<D} Q[i][d] * K[j][d]
+ *        m_i     = max_j S[i][j]
+ *        P[i][j] = exp(S[i][j] - m_i) / sum_{j'} exp(S[i][j'] - m_i)
+ *        O[i][d] = sum_{j<Sk} P[i][j] * V[j][d]
+ *
+ * No mask (the pages name none).  Subtracting the row maximum leaves P
+ * unchanged and keeps exp finite.  Inputs are decoded exactly to double;
+ * every sum is taken in index order, in double.
+ *
+ * Layouts (contiguous): Q [BH][Sq][D], K and V [BH][Sk][D], O [BH][Sq][D]
+ * (double).  dtype 0 = binary16, 1 = bfloat16.  Sk = 0 is refused (a
+ * softmax over no keys is undefined); BH = 0 or Sq = 0 writes nothing.
+ * Return codes: 0 ok, -1 invalid argument or no memory.
+ */
+static int attention_row(int dtype, int64_t Sk, int64_t D, const void* Q, int64_t q_off, const void* K,
+                         const void* V, int64_t kv_off, double scale, double* s, double* o)
+{
+    for (int64_t j = 0; j < Sk; ++j) {
+        double acc = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            acc += decode(dtype, Q, q_off + d) * decode(dtype, K, kv_off + j * D + d);
+        s[j] = scale * acc;
+    }
+    double m = s[0];
+    for (int64_t j = 1; j < Sk; ++j)
+        if (s[j] > m) m = s[j];
+    double z = 0.0;
+    for (int64_t j = 0; j < Sk; ++j) {
+        s[j] = exp(s[j] - m);
+        z += s[j];
+    }
+    for (int64_t j = 0; j < Sk; ++j) s[j] = s[j] / z; /* P[i][j] */
+    for (int64_t d = 0; d < D; ++d) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < Sk; ++j) acc += s[j] * decode(dtype, V, kv_off + j * D + d);
+        o[d] = acc;
+    }
+    return 0;
+}
+
+int oracle_attention(int dtype, int64_t BH, int64_t Sq, int64_t Sk, int64_t D, const void* Q,
+                     const void* K, const void* V, double scale, double* O, int nthreads)
+{
+    if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+    if (BH < 0 || Sq < 0 || Sk <= 0 || D <= 0) return -1;
+    if (BH == 0 || Sq == 0) return 0;
+    int bad = 0;
+    const int nt = set_threads(nthreads);
+#pragma omp parallel num_threads(nt)
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)Sk);
+        if (!s) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(static) collapse(2)
+        for (int64_t b = 0; b < BH; ++b)
+            for (int64_t i = 0; i < Sq; ++i)
+                if (s) attention_row(dtype, Sk, D, Q, (b * Sq + i) * D, K, V, b * Sk * D, scale, s,
+                                     O + (b * Sq + i) * D);
+        free(s);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Selected query rows only: out[e][0..D) = O[slices[e]][rows[e]][0..D). */
+int oracle_attention_rows(int dtype, int64_t BH, int64_t Sq, int64_t Sk, int64_t D, const void* Q,
+                          const void* K, const void* V, double scale, int64_t n_rows, const int64_t* slices,
+                          const int64_t* rows, double* out, int nthreads)
+{
+    if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+    if (BH < 0 || Sq < 0 || Sk <= 0 || D <= 0 || n_rows < 0) return -1;
+    for (int64_t e = 0; e < n_rows; ++e)
+        if (slices[e] < 0 || slices[e] >= BH || rows[e] < 0 || rows[e] >= Sq) return -1;
+    int bad = 0;
+    const int nt = set_threads(nthreads);
+#pragma omp parallel num_threads(nt)
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)Sk);
+        if (!s) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t e = 0; e < n_rows; ++e)
+            if (s) attention_row(dtype, Sk, D, Q, (slices[e] * Sq + rows[e]) * D, K, V, slices[e] * Sk * D, scale,
+                                 s, out + e * D);
+        free(s);
+    }
+    return bad ? -1 : 0;
+}

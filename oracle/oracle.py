@@ -1,4 +1,5 @@
-"""Python face of the CPU oracle (``oracle.c``) for the tiled GEMM C = A*B.
+"""Python face of the CPU oracle (``oracle.c``) for the tiled GEMM C = A*B
+and the attention-style consumer O = softmax(scale Q K^T) V.
 
 TEST INFRASTRUCTURE ONLY: the test-suite, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may use this module; the HIP library and its
@@ -59,8 +60,12 @@ def lib():
         L.oracle_decode_array.argtypes = [i32, vp, i64, vp]
         L.oracle_max_threads.argtypes = []
         L.oracle_scale_by_two.argtypes = [i64, vp, vp]
+        L.oracle_attention.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, ctypes.c_double, vp, i32]
+        L.oracle_attention_rows.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, ctypes.c_double, i64, vp, vp,
+                                            vp, i32]
         for f in ("oracle_gemm_float", "oracle_gemm_float_entries", "oracle_gemm_int8",
-                  "oracle_gemm_int8_entries", "oracle_decode_array", "oracle_max_threads"):
+                  "oracle_gemm_int8_entries", "oracle_decode_array", "oracle_max_threads", "oracle_attention",
+                  "oracle_attention_rows"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -160,6 +165,44 @@ def scale_by_two(x: np.ndarray) -> np.ndarray:
     y = np.empty_like(xb)
     _check(lib().oracle_scale_by_two(xb.size, _ptr(xb), _ptr(y)))
     return y.view(np.float32)
+
+
+def _qkv(Q, K, V, dtype):
+    if dtype not in ("f16", "bf16"):
+        raise TypeError("oracle: attention inputs are f16 or bf16")
+    Qb, Kb, Vb = (_as_bits(np.asarray(x), dtype) for x in (Q, K, V))
+    if Qb.ndim != 3 or Kb.ndim != 3 or Kb.shape != Vb.shape or Qb.shape[0] != Kb.shape[0] or Qb.shape[2] != Kb.shape[2]:
+        raise ValueError("oracle: Q (BH, Sq, D), K and V (BH, Sk, D) expected")
+    return Qb, Kb, Vb
+
+
+def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dtype: str, scale: float,
+              threads: int = 0) -> np.ndarray:
+    """O = softmax(scale * Q K^T) V for each (batch, head) slice, in float64.
+
+    Q (BH, Sq, D), K and V (BH, Sk, D), stored bit patterns of ``dtype``
+    ('f16' or 'bf16'); returns O (BH, Sq, D) float64."""
+    Qb, Kb, Vb = _qkv(Q, K, V, dtype)
+    BH, Sq, D = Qb.shape
+    O = np.zeros((BH, Sq, D), dtype=np.float64)
+    _check(lib().oracle_attention(_DTYPES[dtype], BH, Sq, Kb.shape[1], D, _ptr(Qb), _ptr(Kb), _ptr(Vb),
+                                  float(scale), _ptr(O), threads))
+    return O
+
+
+def attention_rows(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dtype: str, scale: float, slices, rows,
+                   threads: int = 0) -> np.ndarray:
+    """O[slices[e], rows[e], :] for each e (same definition as ``attention``)."""
+    Qb, Kb, Vb = _qkv(Q, K, V, dtype)
+    BH, Sq, D = Qb.shape
+    sl = np.ascontiguousarray(slices, dtype=np.int64)
+    rw = np.ascontiguousarray(rows, dtype=np.int64)
+    if sl.shape != rw.shape or sl.ndim != 1:
+        raise ValueError("slices and rows must be 1-D of the same length")
+    out = np.zeros((sl.size, D), dtype=np.float64)
+    _check(lib().oracle_attention_rows(_DTYPES[dtype], BH, Sq, Kb.shape[1], D, _ptr(Qb), _ptr(Kb), _ptr(Vb),
+                                       float(scale), sl.size, _ptr(sl), _ptr(rw), _ptr(out), threads))
+    return out
 
 
 def max_threads() -> int:

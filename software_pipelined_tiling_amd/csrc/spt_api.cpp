@@ -113,7 +113,22 @@ static void resolve(int dtype, int64_t M, int64_t N, int64_t K, int& variant, in
             if (big && n2 < kCus && n6 <= kCus) tile = 6;
         }
     }
-    if (variant == V_AUTO) variant = V_DIRECT;
+    if (variant == V_AUTO) {
+        variant = V_DIRECT;
+        // One or two K tiles leave the ring nothing to overlap ("Pipeline GPU Kernel",
+        // Schritt 6: K / BK >= 4 amortises the prologue and epilogue).  Where the C store
+        // dominates as well (fp16/bf16/int8 grids of four or more rounds of two workgroups
+        // per CU) the unpipelined loop is faster; elsewhere the ring still is.  MI355X,
+        // medians, us, DIRECT ring -> SYNC: bf16 8192^2 x 32 45.1 -> 44.3, x 64 50.1 ->
+        // 48.9, fp16 8192^2 x 64 50.5 -> 49.1, int8 8192^2 x 128 (B col) 48.5 -> 47.8;
+        // kept: bf16 4096^2 x 64 14.6 (SYNC 15.4), 6144^2 x 64 31.8 (32.5), fp16 8192 x
+        // 4096 x 64 25.3 (26.9), fp32 8192^2 x 32 67.3 (71.4), bf16 8192^2 x 96 52.6 (55.1).
+        const int elt = elt_bytes(dtype);
+        const TileShape& T = kTiles[tile];
+        const int64_t bk = T.BKB / elt, k_tiles = (K + bk - 1) / bk;
+        const int64_t tiles = ((M + T.BM - 1) / T.BM) * ((N + T.BN - 1) / T.BN);
+        if (stages == 0 && elt <= 2 && k_tiles >= 1 && k_tiles <= 2 && tiles >= 8 * kCus) variant = V_SYNC;
+    }
     if (stages == 0)
         stages = variant == V_SYNC ? 1 : variant == V_REG ? 2 : variant == V_PERSIST ? 3 : (kTiles[tile].BKB >= 128 ? 2 : 3);
 }
@@ -172,6 +187,10 @@ static void plan_band(int64_t M, int64_t N, int64_t K, spt_plan_info& p)
     // 260 x 4104 x 4104 42.9 -> 42.8); a band of two per CU keeps 3 (1536 x 5120
     // x 4096: 76.5 against 77.0), and so does bf16 6000^2 x 2000 (AUTO 149.4 us
     // with 3 stages, 157.5 with 4)
+    // The same holds for int8, bf16 and fp32 bands (band rows alone, 128 x 128 tile,
+    // us, 3 -> 4 stages: int8 128 x 4096 x 8192 with column-major B 35.6 -> 30.8, with
+    // row-major B 37.6 -> 37.5; bf16 128 x 4096 x 8192 68.7 -> 60.8, with column-major
+    // B 256 x 4096 x 8192 61.6 -> 53.1; fp32 128 x 4096 x 4096 230.5 -> 230.6).
     p.band_stages = band_grid <= kCus && K * p.elt_bytes >= 8192 ? 4 : 3;
     p.band_m = band_m;
     p.band_grid = band_grid;

@@ -164,7 +164,7 @@ def test_pages_tile_plan(L):
     (spt.I8, 4608, 4608, 4608, spt.ROW, 6, 2),
     (spt.I8, 4096, 4096, 4096, spt.COL, 4, 2),
     (spt.BF16, 8192, 8192, 512, spt.ROW, 1, 3),     # low K: the C store decides
-    (spt.BF16, 8192, 8192, 64, spt.ROW, 1, 3),
+    (spt.BF16, 8192, 8192, 128, spt.ROW, 1, 3),     # four K tiles: the ring
     (spt.F16, 256, 256, 256, spt.ROW, 3, 3),        # too few 128 x 256 tiles for the CUs
     (spt.BF16, 4000, 3000, 1000, spt.ROW, 6, 2),    # 256 x 256 would leave CUs idle in its one
     (spt.BF16, 3000, 3000, 3000, spt.ROW, 6, 2),    # round; 256 x 192 still fits one round
@@ -183,6 +183,31 @@ def test_auto_choice(L, dtype, M, N, K, lay, tile, stages):
     rc, pi = spt.spt_plan(dtype, M, N, K, lay)
     assert rc == 0, spt.spt_last_error()
     assert (pi.tile_id, pi.variant, pi.stages) == (tile, spt.VARIANT_DIRECT, stages)
+
+
+@pytest.mark.parametrize("dtype,M,N,K,lay,variant", [
+    (spt.BF16, 8192, 8192, 32, spt.ROW, spt.VARIANT_SYNC),   # one or two K tiles, four rounds or more
+    (spt.BF16, 8192, 8192, 64, spt.ROW, spt.VARIANT_SYNC),
+    (spt.F16, 8192, 8192, 64, spt.ROW, spt.VARIANT_SYNC),
+    (spt.I8, 8192, 8192, 128, spt.COL, spt.VARIANT_SYNC),
+    (spt.BF16, 8192, 8192, 40, spt.ROW, spt.VARIANT_SYNC),   # one partial K tile
+    (spt.BF16, 4096, 4096, 64, spt.ROW, spt.VARIANT_DIRECT),  # one round
+    (spt.BF16, 6144, 6144, 64, spt.ROW, spt.VARIANT_DIRECT),  # 2.25 rounds
+    (spt.F16, 8192, 4096, 64, spt.ROW, spt.VARIANT_DIRECT),   # two rounds
+    (spt.F32, 8192, 8192, 32, spt.ROW, spt.VARIANT_DIRECT),   # fp32 keeps the ring
+    (spt.BF16, 8192, 8192, 96, spt.ROW, spt.VARIANT_DIRECT),  # three K tiles
+    (spt.BF16, 8192, 8192, 0, spt.ROW, spt.VARIANT_DIRECT),   # nothing to load
+])
+def test_auto_variant_at_short_k(L, dtype, M, N, K, lay, variant):
+    """With one or two K tiles AUTO takes the unpipelined loop where it was measured
+    faster (a store-bound grid of four or more rounds); the ring elsewhere."""
+    rc, pi = spt.spt_plan(dtype, M, N, K, lay)
+    assert rc == 0, spt.spt_last_error()
+    assert pi.variant == variant
+    assert pi.stages == (1 if variant == spt.VARIANT_SYNC else 3)
+    # an explicit stage count or variant is never overridden
+    rc, pi = spt.spt_plan(dtype, M, N, K, lay, spt.VARIANT_AUTO, 3, 0)
+    assert rc == 0 and pi.variant == spt.VARIANT_DIRECT
 
 
 # ---- the persistent variant ---------------------------------------------------
