@@ -129,3 +129,43 @@ def scaled(w: Workload, M: int, N: int, K: int, wid: int | None = None) -> Workl
     """Same dtype / layout / distribution at other sizes (for oracle-sized parity runs)."""
     return Workload(f"{w.name} @ {M}x{N}x{K}", w.wid if wid is None else wid, w.dtype, M, N, K,
                     w.b_col, w.dist, w.lo, w.hi)
+
+
+@dataclass(frozen=True)
+class AttentionWorkload:
+    """One attention problem: BH (batch x heads) slices of Sq queries and Sk keys
+    of head dimension D, entries drawn from `dist` and stored in `dtype`."""
+    name: str
+    wid: int
+    BH: int
+    Sq: int
+    Sk: int
+    D: int
+    dtype: str = "f16"
+    dist: str = "normal"
+    lo: float = -1.0
+    hi: float = 1.0
+
+    @property
+    def flops(self) -> int:
+        """The two products, 4 * BH * Sq * Sk * D ("Kernel-Engpass analysieren", Schritt 1)."""
+        return 4 * self.BH * self.Sq * self.Sk * self.D
+
+    @property
+    def alg_bytes(self) -> int:
+        """Q, K and V read once, the fp32 output written once."""
+        e = ELT_BYTES[self.dtype]
+        return e * self.BH * self.D * (self.Sq + 2 * self.Sk) + 4 * self.BH * self.Sq * self.D
+
+
+def make_qkv(w: AttentionWorkload):
+    """(Q, K, V) host arrays of stored bits: Q (BH, Sq, D), K and V (BH, Sk, D)."""
+    q = draw(w.dist, w.lo, w.hi, (w.BH, w.Sq, w.D), rng_for(w.wid, 0, w.Sk), w.dtype)
+    k = draw(w.dist, w.lo, w.hi, (w.BH, w.Sk, w.D), rng_for(w.wid, 1, w.Sk), w.dtype)
+    v = draw(w.dist, w.lo, w.hi, (w.BH, w.Sk, w.D), rng_for(w.wid, 2, w.Sk), w.dtype)
+    return q, k, v
+
+
+# The attention-style consumer: batch 2 x 16 heads, 4096 queries and keys, head
+# dimension 128, N(0, 1) entries in fp16 (a flash-attention forward shape).
+W_ATTN_4096 = AttentionWorkload("fp16 attention 32 x 4096 x 4096 x 128", 6, 32, 4096, 4096, 128)
