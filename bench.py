@@ -16,6 +16,9 @@ Besides the headline value it reports, in the same line:
                 headline workload, the unpipelined one included
   workloads     int8 4096^3 (B column-major), bf16 8192^2 x K low-K sweep
                 (with HBM GB/s), bf16 4000x3000x1000 ragged, fp16 256^3
+  attention     the attention-style consumer (flash-attention forward, fp16,
+                32 x 4096 x 4096 x 128) under every producer, and the ratio of
+                register-staged to direct-to-LDS time (the pages' high-ratio claim)
   streaming     y = 2x through the S-stage ring: the pages' demonstration
                 (2^20 floats, one block, 3 stages) and 2^28 floats over many
                 blocks, each with the unpipelined S = 1 loop beside it
@@ -273,6 +276,45 @@ def traffic_from_profile(kernel_sha: str):
     if d.get("kernel_source_sha") != kernel_sha:
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+def attention_bench():
+    """The attention-style consumer (spt_attention) on its full-size workload under
+    every producer: the pages' claim is that asynchronous copies stop paying once a
+    tile load feeds many matrix instructions ("Kernel-Engpass analysieren", Schritt 4
+    and the pitfalls: flash attention measured -5% with cp.async)."""
+    import torch
+    import software_pipelined_tiling_amd as spt
+    from software_pipelined_tiling_amd import inputs as I
+    w = I.W_ATTN_4096
+    Q, K, V = (to_dev(x, w.dtype) for x in I.make_qkv(w))
+    O = torch.empty((w.BH, w.Sq, w.D), dtype=torch.float32, device="cuda")
+    scale = 1.0 / w.D ** 0.5
+    res = {"workload": w.name + ", fp32 O, N(0,1) fp16 inputs, scale 1/sqrt(D)", "flop_per_call": w.flops,
+           "alg_bytes_per_call": w.alg_bytes}
+    for v, s_ in [("sync", 1), ("reg", 1), ("reg", 2), ("direct", 2), ("direct", 3), ("auto", 0)]:
+        def fn(stream, v=v, s_=s_):
+            return spt.spt_attention(w.BH, w.Sq, w.Sk, w.D, Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(),
+                                     scale, spt.DTYPE_CODES[w.dtype], stream, spt.VARIANT_CODES[v], s_) == 0
+        us = time_graph(fn, calls=10, reps=5)
+        if us is None:
+            continue
+        tf = w.flops / (us * 1e-6) / 1e12
+        res[f"{v}{s_}"] = {"us": round(us, 2), "tflops": round(tf, 1),
+                           "pct_of_peak": round(100 * tf / PEAK_TFLOPS[w.dtype], 1)}
+    if "direct2" in res and "reg2" in res:
+        best_d = min(res["direct2"]["us"], res["direct3"]["us"])
+        best_r = min(res["reg1"]["us"], res["reg2"]["us"])
+        res["async_over_register_staged"] = {
+            "value": round(best_r / best_d, 3),
+            "what": "time of the best register-staged ring / time of the best direct-to-LDS ring (> 1: the "
+                    "asynchronous copies are faster); the pages measured 0.95 for flash attention on GA104",
+            "pipelined_over_sync": round(res["sync1"]["us"] / min(best_d, best_r), 3)}
+    # the compute/load ratio per key block (spt_attention.hip: 256 query rows, 32 keys of
+    # 128 columns per block, 4 waves): 64 MFMAs per wave per 4 copies per thread
+    res["ratio"] = {"mfma_per_copy": 16.0, "flop_per_byte": 256.0,
+                    "gemm_headline_tile": {"mfma_per_copy": 8.0, "flop_per_byte": 128.0}}
+    return res
 
 
 def stream_bench(steps: int, warmup: int):
@@ -634,6 +676,7 @@ def main():
 
         if not args.only_workload:
             out["streaming"] = stream_bench(steps, 20)
+            out["attention"] = attention_bench()
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(I.W_F16_4096, args.cpu_budget)

@@ -238,6 +238,37 @@ int spt_plan(int dtype, int64_t M, int64_t N, int64_t K,
  */
 int spt_scale_by_two(int64_t n, const void* x, void* y, int stages, int blocks, void* stream);
 
+/*
+ * Attention forward pass, the high-ratio consumer of the same ring: for each
+ * of BH independent (batch, head) slices,
+ *
+ *        O[i][d] = sum_j softmax_j(scale * sum_e Q[i][e] * K[j][e]) * V[j][d]
+ *
+ * (no mask).  "Kernel-Engpass analysieren" uses flash attention as its
+ * example of a kernel with many matrix instructions per tile load (Schritt 4,
+ * and the pitfalls section, where asynchronous copies measured a few percent
+ * slower) and counts its work as 4 * BH * Sq * Sk * D FLOP (Schritt 1).
+ * Key/value blocks stream through the producer `variant` (SPT_VARIANT_SYNC
+ * with 1 stage, SPT_VARIANT_REG with 1-2, SPT_VARIANT_DIRECT with 2-3;
+ * SPT_VARIANT_AUTO / stages 0 = the library's choice), the online softmax
+ * runs in fp32, and the probabilities are rounded to the input type for the
+ * second product.
+ *
+ * dtype SPT_F16 or SPT_BF16 for Q, K, V; O is fp32.  D (head dimension) is 64
+ * or 128.  Layouts (contiguous, DEVICE pointers owned by the caller, 16-byte
+ * aligned): Q [BH][Sq][D], K and V [BH][Sk][D], O [BH][Sq][D].  O must not
+ * overlap Q, K or V.  scale must be finite and >= 0 (the usual 1/sqrt(D) is
+ * the caller's to pass).  Errors: SPT_ERR_INVALID (negative size, Sk = 0 with
+ * work to do -- a softmax over no keys --, null pointer, bad scale, enum
+ * out of range, overlap), SPT_ERR_UNSUPPORTED (dtype, D, a variant/stage
+ * pairing, sizes above 2^31-1, addresses outside the 48-bit range of buffer
+ * descriptors), SPT_ERR_MISALIGNED, SPT_ERR_LAUNCH.  BH = 0 or Sq = 0 returns
+ * SPT_OK without launching.  Asynchronous on `stream`, like spt_gemm.
+ */
+int spt_attention(int64_t BH, int64_t Sq, int64_t Sk, int64_t D,
+                  const void* Q, const void* K, const void* V, void* O,
+                  float scale, int dtype, void* stream, int variant, int stages);
+
 /* Static string naming a status code. */
 const char* spt_status_string(int status);
 

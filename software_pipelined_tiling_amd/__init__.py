@@ -15,7 +15,7 @@ import os
 
 __all__ = [
     "spt_gemm", "spt_gemm_ex", "spt_plan", "spt_status_string", "spt_last_error", "spt_version",
-    "spt_scale_by_two", "gemm", "plan", "scale_by_two", "SptError", "PlanInfo", "lib_path",
+    "spt_scale_by_two", "spt_attention", "attention", "gemm", "plan", "scale_by_two", "SptError", "PlanInfo", "lib_path",
     "F16", "BF16", "I8", "F32", "ROW", "COL", "VARIANT_AUTO", "VARIANT_SYNC", "VARIANT_REG",
     "VARIANT_DIRECT", "VARIANT_PERSIST", "TILE_AUTO", "TILE_128x256", "TILE_256x256", "TILE_128x128", "TILE_256x256_4W",
     "TILE_256x256_4W_K64B", "TILE_256x192",
@@ -92,6 +92,8 @@ def _load():
         L.spt_version.restype = i32
         L.spt_scale_by_two.argtypes = [i64, vp, vp, i32, i32, vp]
         L.spt_scale_by_two.restype = i32
+        L.spt_attention.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, ctypes.c_float, i32, vp, i32, i32]
+        L.spt_attention.restype = i32
         _lib = L
     return _lib
 
@@ -122,6 +124,10 @@ def spt_plan(dtype, M, N, K, b_layout=ROW, variant=VARIANT_AUTO, stages=0, tile_
 
 def spt_scale_by_two(n, x, y, stages=0, blocks=0, stream=0) -> int:
     return _load().spt_scale_by_two(n, x, y, stages, blocks, stream)
+
+
+def spt_attention(BH, Sq, Sk, D, Q, K, V, O, scale, dtype, stream=0, variant=VARIANT_AUTO, stages=0) -> int:
+    return _load().spt_attention(BH, Sq, Sk, D, Q, K, V, O, scale, dtype, stream, variant, stages)
 
 
 def spt_status_string(status: int) -> str:
@@ -201,6 +207,38 @@ def gemm(A, B, out=None, *, b_layout: str = "row", variant: str = "auto", stages
                          tile)
     if rc != SPT_OK:
         raise SptError(rc, "spt_gemm_ex")
+    return out
+
+
+def attention(Q, K, V, scale: float | None = None, out=None, *, variant: str = "auto", stages: int = 0,
+              stream=None):
+    """O = softmax(scale * Q K^T) V for contiguous fp16/bf16 torch tensors on the GPU
+    (Q (BH, Sq, D), K and V (BH, Sk, D)), through ``spt_attention``; O is fp32.
+    `scale` defaults to 1/sqrt(D)."""
+    import torch
+    if Q.dtype != K.dtype or Q.dtype != V.dtype or Q.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("Q, K, V must share one dtype, float16 or bfloat16")
+    if Q.dim() != 3 or K.dim() != 3 or K.shape != V.shape or K.shape[0] != Q.shape[0] or K.shape[2] != Q.shape[2]:
+        raise ValueError("Q (BH, Sq, D), K and V (BH, Sk, D) expected")
+    if not (Q.is_contiguous() and K.is_contiguous() and V.is_contiguous()):
+        raise ValueError("Q, K, V must be contiguous")
+    if not Q.is_cuda or K.device != Q.device or V.device != Q.device:
+        raise ValueError("Q, K, V must be on the same GPU")
+    BH, Sq, D = Q.shape
+    Sk = K.shape[1]
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    if out is None:
+        out = torch.empty((BH, Sq, D), dtype=torch.float32, device=Q.device)
+    if out.dtype != torch.float32 or out.shape != (BH, Sq, D) or not out.is_contiguous() or out.device != Q.device:
+        raise ValueError("out must be a contiguous float32 (BH, Sq, D) tensor on Q's GPU")
+    if stream is None:
+        stream = torch.cuda.current_stream(Q.device).cuda_stream
+    with torch.cuda.device(Q.device):
+        rc = spt_attention(BH, Sq, Sk, D, Q.data_ptr(), K.data_ptr(), V.data_ptr(), out.data_ptr(), scale,
+                           _torch_dtype_code(Q), stream, VARIANT_CODES[variant], stages)
+    if rc != SPT_OK:
+        raise SptError(rc, "spt_attention")
     return out
 
 

@@ -19,7 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = [f"spt_kernels_{dt}_{lay}.hip" for dt in ("f16", "bf16", "i8", "f32") for lay in ("row", "col")]
-SOURCES += ["spt_stream.hip", "spt_api.cpp"]
+SOURCES += ["spt_stream.hip", "spt_attention.hip", "spt_api.cpp"]
 HEADERS = ["spt_kernel.hpp", "spt_persist.hpp", "spt_instances.hpp", "spt_registry.h", "spt_config.h"]
 
 # Packed-fp32 VALU instructions are disabled for all device code (-packed-fp32-ops).
@@ -94,7 +94,7 @@ def build_poison(verbose: bool = True) -> str:
         f.write('#include "spt_registry.h"\nnamespace spt {\n')
         f.writelines(f"KernelTable kernels_{t}() {{ return KernelTable{{nullptr, 0}}; }}\n" for t in empty)
         f.write("}\n")
-    srcs = [f"spt_kernels_{t}.hip" for t in POISON_TABLES] + ["spt_stream.hip", "spt_api.cpp"]
+    srcs = [f"spt_kernels_{t}.hip" for t in POISON_TABLES] + ["spt_stream.hip", "spt_attention.hip", "spt_api.cpp"]
     with cf.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
         objs = list(ex.map(lambda s: _compile(s, ("SPT_POISON",), "_poison"), srcs))
     stub_obj = os.path.join(BUILD, "spt_poison_stub.o")

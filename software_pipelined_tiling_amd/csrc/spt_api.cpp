@@ -433,6 +433,46 @@ static int scale_by_two_impl(int64_t n, const void* x, void* y, int stages, int 
     return SPT_OK;
 }
 
+// The attention-style consumer: validation, then one launch.
+static int attention_impl(int64_t BH, int64_t Sq, int64_t Sk, int64_t D, const void* Q, const void* K,
+                          const void* V, void* O, float scale, int dtype, void* stream, int variant, int stages)
+{
+    if (dtype != DT_F16 && dtype != DT_BF16) return fail(SPT_ERR_UNSUPPORTED, "attention: dtype %d (f16, bf16)", dtype);
+    if (variant < 0 || variant > 3) return fail(SPT_ERR_INVALID, "variant %d is not a producer", variant);
+    if (stages < 0 || stages > 4) return fail(SPT_ERR_INVALID, "stages %d not in 0..4", stages);
+    if (BH < 0 || Sq < 0 || Sk < 0 || D < 0) return fail(SPT_ERR_INVALID, "negative size");
+    if (!(scale >= 0.0f) || scale > 3.0e38f) return fail(SPT_ERR_INVALID, "scale must be finite and >= 0");
+    // AUTO: the DIRECT ring of three stages (measured the fastest producer at 4096 keys)
+    if (variant == V_AUTO) variant = V_DIRECT;
+    if (stages == 0) stages = variant == V_SYNC ? 1 : variant == V_REG ? 2 : 3;
+    if (!((variant == V_SYNC && stages == 1) || (variant == V_REG && (stages == 1 || stages == 2)) ||
+          (variant == V_DIRECT && (stages == 2 || stages == 3))))
+        return fail(SPT_ERR_UNSUPPORTED, "attention: variant %d has no %d-stage form", variant, stages);
+    if (D != 64 && D != 128) return fail(SPT_ERR_UNSUPPORTED, "attention: head dimension %lld (64, 128)", (long long)D);
+    if (BH == 0 || Sq == 0) return SPT_OK;
+    if (Sk == 0) return fail(SPT_ERR_INVALID, "attention over no keys (a softmax over an empty row)");
+    if (Sq > INT32_MAX || Sk > INT32_MAX || BH > INT32_MAX) return fail(SPT_ERR_UNSUPPORTED, "size above 2^31-1");
+    if ((uint64_t)BH * (uint64_t)Sq > (UINT64_C(1) << 40) || (uint64_t)BH * (uint64_t)Sk > (UINT64_C(1) << 40))
+        return fail(SPT_ERR_UNSUPPORTED, "Q, K or V above 2^40 rows");
+    if (BH * ((Sq + 255) / 256) > INT32_MAX) return fail(SPT_ERR_UNSUPPORTED, "too many workgroups");
+    if (!Q || !K || !V || !O) return fail(SPT_ERR_INVALID, "Q, K, V or O is null");
+    if ((uintptr_t)Q % 16 || (uintptr_t)K % 16 || (uintptr_t)V % 16 || (uintptr_t)O % 16)
+        return fail(SPT_ERR_MISALIGNED, "Q, K, V or O not 16-byte aligned");
+    const uintptr_t hi = (uintptr_t)1 << 47;
+    const uintptr_t q0 = (uintptr_t)Q, k0 = (uintptr_t)K, v0 = (uintptr_t)V, o0 = (uintptr_t)O;
+    const uintptr_t q1 = q0 + (uintptr_t)(BH * Sq * D * 2), k1 = k0 + (uintptr_t)(BH * Sk * D * 2),
+                    v1 = v0 + (uintptr_t)(BH * Sk * D * 2), o1 = o0 + (uintptr_t)(BH * Sq * D * 4);
+    if (q0 < 65536 || k0 < 65536 || v0 < 65536 || q1 > hi || k1 > hi || v1 > hi)
+        return fail(SPT_ERR_UNSUPPORTED, "Q, K or V outside the device address range of buffer descriptors");
+    if ((o0 < q1 && q0 < o1) || (o0 < k1 && k0 < o1) || (o0 < v1 && v0 < o1))
+        return fail(SPT_ERR_INVALID, "O overlaps Q, K or V");
+    const double c = (double)scale * 1.4426950408889634;  // log2(e)
+    const hipError_t err = launch_attention(dtype, (int)D, variant, stages, Q, K, V, O, (int)BH, (int)Sq, (int)Sk,
+                                            (float)c, (hipStream_t)stream);
+    if (err != hipSuccess) return fail(SPT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(err));
+    return SPT_OK;
+}
+
 // Every entry point returns through here: the thread's message describes its
 // most recent call, and is empty when that call succeeded.
 static int done(int status)
@@ -444,6 +484,13 @@ static int done(int status)
 }  // namespace spt
 
 extern "C" {
+
+int spt_attention(int64_t BH, int64_t Sq, int64_t Sk, int64_t D, const void* Q, const void* K, const void* V,
+                  void* O, float scale, int dtype, void* stream, int variant, int stages)
+{
+    return spt::done(spt::attention_impl(BH, Sq, Sk, D, Q, K, V, O, scale, dtype, stream, variant, stages));
+}
+
 
 int spt_scale_by_two(int64_t n, const void* x, void* y, int stages, int blocks, void* stream)
 {

@@ -1,0 +1,545 @@
+// spt_attention.hip -- the attention-style consumer of the K/V ring: a
+// flash-attention forward pass, O = softmax(scale * Q K^T) V, for gfx950.
+//
+// "Kernel-Engpass analysieren" uses flash attention as its high-ratio kernel:
+// many matrix instructions per tile load (Schritt 4), so that long compute
+// phases already hide the load latency and asynchronous copies stop paying
+// (the pitfalls section reports them a few percent slower there).  This file
+// streams blocks of keys and values through the same three producers as the
+// GEMM K-loop (spt_kernel.hpp), so the claim can be measured here:
+//
+//  V_SYNC    load -> barrier -> compute -> barrier, one LDS stage;
+//  V_REG     block t+1 fetched global -> VGPR while block t is computed, then
+//            written to LDS (S = 1 or 2 stages); the fetch is issued once block
+//            t's S = Q K^T is done, when the registers it needs are free;
+//  V_DIRECT  buffer_load_dwordx4 ... lds copies into an S-stage ring (S = 2
+//            or 3): wait -> barrier -> copies of block t+S-1 into the stage
+//            just freed -> compute block t ("Hiding Memory Latency in CUDA:
+//            Asynchronous Loads and Software Pipelines", sections 3-5).
+//
+// One workgroup of 4 waves owns 256 query rows of one (batch, head) slice;
+// each wave owns 64 rows, whose Q fragments stay in registers for the whole
+// kernel.  For every block of BKV keys (64; 32 with 128 columns, whose
+// accumulators leave fewer registers) a wave computes
+//     S = Q K^T           (16 x v_mfma_f32_16x16x32 per 32-wide d-step),
+//     the online softmax  (a reference row maximum m, the running sum l, and a
+//                          rescale of the output accumulators by 2^(m_old - m_new)
+//                          when m moves),
+//     O += P V            (P rounded to the input type, 16-bit MFMAs),
+// and finally writes O / l in fp32.  Exponentials are base 2 with log2(e)
+// folded into the scale.
+//
+// MFMA layouts (operands swapped as in the GEMM: the K or V fragment is the
+// first operand).  S block (m, n): lane (g = lane/16, i = lane%16) holds query
+// row 16m + i, keys 16n + 4g + 0..3.  The P fragment of key-step u takes, in
+// this order, the keys 32u + 4g + 0..3 and 32u + 16 + 4g + 0..3 of its row --
+// an MFMA may contract its 32 k values in any order, as long as the V
+// fragment supplies the same keys in the same positions: two transposing
+// ds_read_b64_tr_b16 reads at key rows 32u + 4g + (i/4) and 32u + 16 + 4g +
+// (i/4).  O block (m, n): lane holds query row 16m + i, columns 16n + 4g + 0..3
+// (one 16-byte store).
+//
+// LDS stage: the K block (64 rows of 2D bytes) then the V block.  K rows are
+// read 16 at a time at one 16-byte chunk (ds_read_b128), so chunk c of row r
+// sits at c ^ (r' mod chunks) with r' = r / (rows per 256-byte bank line); V is
+// read by 16 rows x 32 bytes (the transposing reads), so its chunk pairs are
+// XOR-ed by (r' mod pairs).  The producer computes which global chunk belongs
+// at each position; a copy of one wave moves 1 KiB of whole rows.
+//
+// Edges.  Keys past Sk: the last block's descriptor ends at the slice, so its
+// copies read zeros there, and those keys get weight 0 (their logits are -inf).
+// Query rows past Sq read zeros and are never stored.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "spt_kernel.hpp"
+#include "spt_registry.h"
+
+namespace spt {
+
+struct AttnArgs {
+    const char* Q;
+    const char* K;
+    const char* V;
+    char* O;
+    int BH, Sq, Sk;
+    int q_blocks;  // ceil(Sq / 256)
+    int kv_blocks; // ceil(Sk / BKV)
+    float c;       // scale * log2(e)
+};
+
+template <int DT_, int D_, int V_, int S_>
+struct AttnCfg {
+    static constexpr int DT = DT_, D = D_, V = V_, S = S_;
+    static constexpr int WAVES = 4, THREADS = 256;
+    static constexpr int WQ = 64, BQ = WAVES * WQ;  // query rows per wave / per workgroup
+    static constexpr int BKV = D_ == 128 ? 32 : 64;  // keys per block (128 columns: 32, for registers)
+    static constexpr int FM = WQ / 16;              // 16-row query blocks per wave
+    static constexpr int NB = BKV / 16;             // 16-key blocks per key block
+    static constexpr int KS = D / 32;               // d-steps of Q K^T
+    static constexpr int US = BKV / 32;             // key-steps of P V
+    static constexpr int DN = D / 16;               // 16-column blocks of O
+    static constexpr int RB = D * 2;                // bytes per row of Q, K, V
+    static constexpr int NCH = RB / 16;             // 16-byte chunks per row
+    static constexpr int RPL = 256 / RB;            // rows per 256-byte bank line
+    static constexpr int KV_BYTES = BKV * RB;       // one K (or V) block
+    static constexpr int STAGE_BYTES = 2 * KV_BYTES;
+    static constexpr int LDS_BYTES = S * STAGE_BYTES;
+    static constexpr int CPW = KV_BYTES / 1024 / WAVES;  // 1 KiB copies per wave per operand
+    static constexpr int LOADS = 2 * CPW;                // copies per thread per block
+    static_assert(D == 64 || D == 128, "head dimension 64 or 128");
+    static_assert(CPW >= 1 && CPW <= 4, "a wave's copies of one operand share one M0 value");
+    static_assert(V_ != V_SYNC || S_ == 1, "SYNC has one stage");
+    static_assert(V_ != V_REG || S_ == 1 || S_ == 2, "REG has 1 or 2 stages");
+    static_assert(V_ != V_DIRECT || S_ == 2 || S_ == 3, "DIRECT has 2 or 3 stages");
+    static_assert(LDS_BYTES <= kLdsPerCu, "LDS ring exceeds 160 KiB");
+    static_assert((S_ - 1) * LOADS < 64, "vmcnt range");
+};
+
+template <class C>
+struct Attn {
+    typedef f32x4_t acc_t;
+    // How far (in the base-2 logit domain) a row's maximum may exceed the reference
+    // before the reference moves: probabilities stay below 2^8, well inside fp16.
+    static constexpr float kSlack = 8.0f;
+
+    static __device__ __forceinline__ constexpr int swz_k(int r) { return (r / C::RPL) & (C::NCH - 1); }
+    static __device__ __forceinline__ constexpr int swz_v(int r) { return ((r / C::RPL) & (C::NCH / 2 - 1)) << 1; }
+
+    // Global byte offset (from the block's first row) of the chunk that sits at LDS
+    // byte p of the K (or V) region.
+    template <bool IS_V>
+    static __device__ __forceinline__ int src_of(int p)
+    {
+        const int r = p / C::RB, pc = (p % C::RB) / 16;
+        const int lc = pc ^ (IS_V ? swz_v(r) : swz_k(r));
+        return r * C::RB + lc * 16;
+    }
+
+    // Copies go in groups that share one M0 value: copy j adds the immediate j KiB
+    // to its LDS and global address, so its register offset is lowered by as much
+    // and raised by BIAS (the descriptor base is lowered by BIAS).
+    static constexpr int BIAS = 3072;
+
+    struct Copy {
+        int goff[C::LOADS];  // global offset of copy j (K copies first, then V) within its block
+    };
+
+    static __device__ __forceinline__ i32x4_t desc(uint64_t base, uint32_t bytes)
+    {
+        return (i32x4_t){__builtin_amdgcn_readfirstlane((int)(uint32_t)base),
+                         __builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32)),
+                         __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+    }
+
+    // Key block t of this slice: the addresses of its first K and V rows and the bytes
+    // readable from them (up to the end of the slice, at most one block; zero past
+    // the last block).
+    static __device__ __forceinline__ void block_span(const AttnArgs& p, int slice, int t, const char*& kb,
+                                                      const char*& vb, uint32_t& ext)
+    {
+        const long long row0 = (long long)slice * p.Sk + (long long)t * C::BKV;
+        const int rows = t < p.kv_blocks ? min(C::BKV, p.Sk - t * C::BKV) : 0;
+        ext = (uint32_t)(max(rows, 0) * C::RB);
+        kb = p.K + row0 * C::RB;
+        vb = p.V + row0 * C::RB;
+    }
+    // DIRECT descriptors of block t: bases lowered by BIAS (the register offsets are
+    // raised by as much), extents raised by it; zero extent past the last block.
+    static __device__ __forceinline__ void block_desc(const AttnArgs& p, int slice, int t, i32x4_t& dk, i32x4_t& dv)
+    {
+        const char *kb, *vb;
+        uint32_t ext;
+        block_span(p, slice, t, kb, vb, ext);
+        const uint32_t e = ext > 0 ? ext + BIAS : 0u;
+        dk = desc((uint64_t)(uintptr_t)kb - BIAS, e);
+        dv = desc((uint64_t)(uintptr_t)vb - BIAS, e);
+    }
+
+    // DIRECT: the copies of one block into the stage at LDS byte address `st`.
+    static __device__ __forceinline__ void dma_block(const Copy& cp, i32x4_t dk, i32x4_t dv, uint32_t st, int wave)
+    {
+        const uint32_t mk = st + (uint32_t)(wave * C::CPW) * 1024u;
+        const uint32_t mv = mk + (uint32_t)C::KV_BYTES;
+        static_for<0, C::CPW>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            dma16<j * 1024, j == 0>(dk, mk, cp.goff[j] - j * 1024 + BIAS);
+        });
+        static_for<0, C::CPW>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            dma16<j * 1024, j == 0>(dv, mv, cp.goff[C::CPW + j] - j * 1024 + BIAS);
+        });
+    }
+
+    // REG / SYNC: the same chunks through VGPRs.
+    static __device__ __forceinline__ void load_block(const AttnArgs& p, int slice, int t, const Copy& cp,
+                                                      i32x4_t (&r)[C::LOADS])
+    {
+        const char *kb, *vb;
+        uint32_t ext;
+        block_span(p, slice, t, kb, vb, ext);
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, ext), rv = make_rsrc(vb, ext);
+#pragma unroll
+        for (int j = 0; j < C::CPW; ++j) r[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, cp.goff[j], 0, 0);
+#pragma unroll
+        for (int j = 0; j < C::CPW; ++j)
+            r[C::CPW + j] = __builtin_amdgcn_raw_buffer_load_b128(rv, cp.goff[C::CPW + j], 0, 0);
+    }
+    static __device__ __forceinline__ void store_block(SPT_LDS char* st, int wave, int lane,
+                                                       const i32x4_t (&r)[C::LOADS])
+    {
+#pragma unroll
+        for (int j = 0; j < C::CPW; ++j)
+            *(SPT_LDS i32x4_t*)(st + (wave * C::CPW + j) * 1024 + 16 * lane) = r[j];
+#pragma unroll
+        for (int j = 0; j < C::CPW; ++j)
+            *(SPT_LDS i32x4_t*)(st + C::KV_BYTES + (wave * C::CPW + j) * 1024 + 16 * lane) = r[C::CPW + j];
+    }
+
+    // Per-lane LDS offsets of the fragment reads (row 0 of each fragment; other
+    // rows add an immediate).
+    struct Lanes {
+        int k[C::KS];   // K fragment of d-step s (16 key rows x one chunk)
+        int v[C::DN];   // V fragment of column block n (first transposing read)
+    };
+    static __device__ void setup_lanes(int lane, Lanes& L)
+    {
+        const int g = lane >> 4, i = lane & 15;
+        // swz_k(16 n + i) == swz_k(i) and swz_v(32 u + 16 h + r) == swz_v(r): the block
+        // offsets never reach the XOR bits
+#pragma unroll
+        for (int s = 0; s < C::KS; ++s) L.k[s] = i * C::RB + 16 * ((4 * s + g) ^ swz_k(i));
+        const int r = 4 * g + (i >> 2);
+#pragma unroll
+        for (int n = 0; n < C::DN; ++n)
+            L.v[n] = C::KV_BYTES + r * C::RB + 16 * ((2 * n + ((i & 3) >> 1)) ^ swz_v(r)) + 8 * (i & 1);
+    }
+
+    static __device__ __forceinline__ i32x4_t read_k(const SPT_LDS char* st, const Lanes& L, int n, int s)
+    {
+        return *(const SPT_LDS i32x4_t*)(st + L.k[s] + 16 * n * C::RB);
+    }
+    static __device__ __forceinline__ i32x4_t read_v(const SPT_LDS char* st, const Lanes& L, int n, int u)
+    {
+        const int o0 = L.v[n] + 32 * u * C::RB;
+        const int o1 = o0 + 16 * C::RB;
+        {  // (bf16 moves the same 16-bit patterns)
+            typedef __fp16 raw4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+            const raw4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((SPT_LDS raw4*)(st + o0));
+            const raw4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((SPT_LDS raw4*)(st + o1));
+            const i32x2_t l2 = __builtin_bit_cast(i32x2_t, lo), h2 = __builtin_bit_cast(i32x2_t, hi);
+            return (i32x4_t){l2.x, l2.y, h2.x, h2.y};
+        }
+    }
+
+    // Two probabilities -> one 32-bit word of the input type (round to nearest even).
+    static __device__ __forceinline__ int pack2(float a, float b)
+    {
+        if constexpr (C::DT == DT_F16) {
+            typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+            return __builtin_bit_cast(int, (h2){(_Float16)a, (_Float16)b});
+        } else {
+            typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+            return __builtin_bit_cast(int, (b2){(__bf16)a, (__bf16)b});
+        }
+    }
+
+    static __device__ __forceinline__ float xmax(float v)
+    {
+        v = fmaxf(v, __shfl_xor(v, 16));
+        return fmaxf(v, __shfl_xor(v, 32));
+    }
+    static __device__ __forceinline__ float xsum(float v)
+    {
+        v += __shfl_xor(v, 16);
+        return v + __shfl_xor(v, 32);
+    }
+
+    // One key block from the stage at `st`: S = Q K^T, online softmax, O += P V.
+    // `mid` runs between S = Q K^T and the softmax, once the K fragments are dead.
+    template <class F>
+    static __device__ __forceinline__ void block(const AttnArgs& p, const SPT_LDS char* st, const Lanes& L,
+                                                 const i32x4_t (&qf)[C::FM][C::KS], acc_t (&o)[C::FM][C::DN],
+                                                 float (&mrun)[C::FM], float (&lrun)[C::FM], int t, int lane, F&& mid)
+    {
+        acc_t s[C::FM][C::NB];
+#pragma unroll
+        for (int m = 0; m < C::FM; ++m)
+#pragma unroll
+            for (int n = 0; n < C::NB; ++n) s[m][n] = (acc_t){0, 0, 0, 0};
+        // S = Q K^T over the (d-step, key block) fragments in order, each read two
+        // fragments ahead of its MFMAs
+        constexpr int NK = C::KS * C::NB;
+        i32x4_t kf[3];
+        kf[0] = read_k(st, L, 0, 0);
+        kf[1] = read_k(st, L, 1 % C::NB, 1 / C::NB);
+        static_for<0, NK>([&](auto fc) {
+            constexpr int f = decltype(fc)::value;
+            if constexpr (f + 2 < NK) kf[(f + 2) % 3] = read_k(st, L, (f + 2) % C::NB, (f + 2) / C::NB);
+#pragma unroll
+            for (int m = 0; m < C::FM; ++m) mma<C::DT>(s[m][f % C::NB], kf[f % 3], qf[m][f / C::NB]);
+        });
+
+        mid();
+
+        // logits x = c * S in the base-2 domain; keys past Sk get -inf
+#pragma unroll
+        for (int m = 0; m < C::FM; ++m)
+#pragma unroll
+            for (int n = 0; n < C::NB; ++n) s[m][n] *= p.c;  // logits, then probabilities, in place
+        if (t * C::BKV + C::BKV > p.Sk) {  // the ragged last block (wave-uniform)
+            const int lim = p.Sk - t * C::BKV - 4 * (lane >> 4);  // keys 16 n + e < lim are inside Sk
+#pragma unroll
+            for (int m = 0; m < C::FM; ++m)
+#pragma unroll
+                for (int n = 0; n < C::NB; ++n)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (16 * n + e >= lim) s[m][n][e] = -INFINITY;
+        }
+        float bmax[C::FM];
+        bool up = false;
+#pragma unroll
+        for (int m = 0; m < C::FM; ++m) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int n = 0; n < C::NB; ++n)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[m][n][e]);
+            bmax[m] = xmax(mx);
+            up |= bmax[m] > mrun[m] + kSlack;
+        }
+        // The reference maximum of a row moves only when a block's maximum exceeds it
+        // by more than kSlack (always in the first block): the probabilities are taken
+        // relative to the reference, so they stay below 2^kSlack, and the output rows
+        // and sums are rescaled by 2^(old - new) only then -- a wave-uniform branch
+        // that data with a steady maximum skips after the first block.  Any reference
+        // gives the same softmax; this one saves the rescale of 128 accumulators per
+        // block.
+        if (__builtin_amdgcn_ballot_w64(up)) {
+#pragma unroll
+            for (int m = 0; m < C::FM; ++m) {
+                const float mnew = bmax[m] > mrun[m] + kSlack ? bmax[m] : mrun[m];
+                const float alpha = __builtin_amdgcn_exp2f(mrun[m] - mnew);  // 0 in the first block
+                mrun[m] = mnew;
+                lrun[m] *= alpha;
+#pragma unroll
+                for (int n = 0; n < C::DN; ++n) o[m][n] *= alpha;
+            }
+        }
+        i32x4_t pf[C::FM][C::US];
+#pragma unroll
+        for (int m = 0; m < C::FM; ++m) {
+            acc_t (&x)[C::NB] = s[m];
+            float sum = 0.f;
+#pragma unroll
+            for (int n = 0; n < C::NB; ++n)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[n][e] = __builtin_amdgcn_exp2f(x[n][e] - mrun[m]);
+                    sum += x[n][e];
+                }
+            lrun[m] += sum;
+#pragma unroll
+            for (int u = 0; u < C::US; ++u)
+                pf[m][u] = (i32x4_t){pack2(x[2 * u][0], x[2 * u][1]), pack2(x[2 * u][2], x[2 * u][3]),
+                                     pack2(x[2 * u + 1][0], x[2 * u + 1][1]), pack2(x[2 * u + 1][2], x[2 * u + 1][3])};
+        }
+
+        // O += P V over the (key-step, column block) fragments in order, each read
+        // two fragments ahead of its MFMAs
+        constexpr int NF = C::US * C::DN;
+        i32x4_t vf[3];
+        vf[0] = read_v(st, L, 0, 0);
+        vf[1] = read_v(st, L, 1 % C::DN, 1 / C::DN);
+        static_for<0, NF>([&](auto fc) {
+            constexpr int f = decltype(fc)::value;
+            if constexpr (f + 2 < NF) vf[(f + 2) % 3] = read_v(st, L, (f + 2) % C::DN, (f + 2) / C::DN);
+#pragma unroll
+            for (int m = 0; m < C::FM; ++m) mma<C::DT>(o[m][f % C::DN], vf[f % 3], pf[m][f / C::DN]);
+        });
+    }
+
+    // XCD-aware placement: workgroups are dispatched round-robin over the 8 XCDs;
+    // renumber so that each XCD gets a contiguous run, in which consecutive
+    // workgroups are query blocks of one slice (they share its K and V in that
+    // XCD's L2).
+    static __device__ __forceinline__ void place(int bid, int total, int q_blocks, int& slice, int& qb)
+    {
+        const int q = total / 8, rem = total % 8;
+        const int xcd = bid % 8, j = bid / 8;
+        const int id = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + j;
+        slice = id / q_blocks;
+        qb = id - slice * q_blocks;
+    }
+
+    static __device__ __forceinline__ void run(const AttnArgs& p)
+    {
+        __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS_BYTES];
+        SPT_LDS char* smem = (SPT_LDS char*)smem_raw;
+        const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+        const int tid = threadIdx.x, lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int g = lane >> 4, i = lane & 15;
+        int slice_, qb_;
+        place(blockIdx.x, p.BH * p.q_blocks, p.q_blocks, slice_, qb_);
+        const int slice = __builtin_amdgcn_readfirstlane(slice_), qb = __builtin_amdgcn_readfirstlane(qb_);
+        const int qw = qb * C::BQ + wave * C::WQ;  // this wave's first query row
+
+        // Q fragments (m, s): row 16 m + i, chunk 4 s + g; rows past Sq read zeros
+        i32x4_t qf[C::FM][C::KS];
+        {
+            const long long row0 = (long long)slice * p.Sq + qw;
+            const int rows = max(0, min(C::WQ, p.Sq - qw));
+            const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.Q + row0 * C::RB, (uint32_t)(rows * C::RB));
+#pragma unroll
+            for (int m = 0; m < C::FM; ++m)
+#pragma unroll
+                for (int s = 0; s < C::KS; ++s)
+                    qf[m][s] = __builtin_amdgcn_raw_buffer_load_b128(rq, (16 * m + i) * C::RB + (4 * s + g) * 16, 0, 0);
+            // The Q fragments are only ever MFMA operands, which may sit in the
+            // accumulator registers: keep them there, off the VGPRs the softmax and
+            // the register-staged fetch need.
+#pragma unroll
+            for (int m = 0; m < C::FM; ++m)
+#pragma unroll
+                for (int s = 0; s < C::KS; ++s) asm volatile("" : "+a"(qf[m][s]));
+        }
+
+        Copy cp;
+#pragma unroll
+        for (int j = 0; j < C::CPW; ++j) {
+            cp.goff[j] = src_of<false>((wave * C::CPW + j) * 1024 + 16 * lane);
+            cp.goff[C::CPW + j] = src_of<true>((wave * C::CPW + j) * 1024 + 16 * lane);
+        }
+        Lanes L;
+        setup_lanes(lane, L);
+
+        acc_t o[C::FM][C::DN];
+        float mrun[C::FM], lrun[C::FM];
+#pragma unroll
+        for (int m = 0; m < C::FM; ++m) {
+            mrun[m] = -INFINITY;
+            lrun[m] = 0.f;
+#pragma unroll
+            for (int n = 0; n < C::DN; ++n) o[m][n] = (acc_t){0, 0, 0, 0};
+        }
+
+        const int nb = p.kv_blocks;
+        if constexpr (C::V == V_DIRECT) {
+            i32x4_t dk, dv;
+            // prologue: blocks 0 .. S-2 into stages 0 .. S-2
+#pragma unroll
+            for (int b = 0; b < C::S - 1; ++b) {
+                block_desc(p, slice, b, dk, dv);
+                dma_block(cp, dk, dv, lds0 + b * C::STAGE_BYTES, wave);
+            }
+            uint32_t rs = 0;                                   // stage of block t
+            uint32_t ws = (C::S - 1) * C::STAGE_BYTES;         // stage of block t + S - 1
+            for (int t = 0; t < nb; ++t) {
+                wait_lgkmcnt0();                              // this wave's reads of block t-1 are done
+                wait_vmcnt<(C::S - 2) * C::LOADS>();          // its copies of block t have landed
+                barrier();                                    // block t visible; the stage of t-1 free
+                block_desc(p, slice, t + C::S - 1, dk, dv);
+                dma_block(cp, dk, dv, lds0 + ws, wave);       // block t+S-1 into that stage
+                block(p, smem + rs, L, qf, o, mrun, lrun, t, lane, [] {});
+                rs = rs + C::STAGE_BYTES == (uint32_t)C::LDS_BYTES ? 0u : rs + C::STAGE_BYTES;
+                ws = ws + C::STAGE_BYTES == (uint32_t)C::LDS_BYTES ? 0u : ws + C::STAGE_BYTES;
+            }
+            wait_vmcnt<0>();  // no copy may still be writing this workgroup's LDS
+        } else if constexpr (C::V == V_REG) {
+            i32x4_t r[C::LOADS];
+            if (nb > 0) {  // prologue: block 0 into stage 0
+                load_block(p, slice, 0, cp, r);
+                wait_vmcnt<0>();
+                store_block(smem, wave, lane, r);
+                wait_lgkmcnt0();
+                barrier();
+            }
+            for (int t = 0; t < nb; ++t) {
+                SPT_LDS char* cur = smem + (C::S == 2 ? (t & 1) : 0) * C::STAGE_BYTES;
+                SPT_LDS char* nxt = smem + (C::S == 2 ? ((t + 1) & 1) : 0) * C::STAGE_BYTES;
+                // block t+1 is fetched while block t is computed: issued once S = Q K^T is
+                // done (before it, the K fragments hold the registers the fetch needs),
+                // in flight over the softmax and O += P V (past the end: zero-length, zeros)
+                block(p, cur, L, qf, o, mrun, lrun, t, lane, [&] { load_block(p, slice, t + 1, cp, r); });
+                if constexpr (C::S == 1) barrier();       // one buffer: every read of it done first
+                wait_vmcnt<0>();
+                store_block(nxt, wave, lane, r);
+                wait_lgkmcnt0();
+                barrier();
+            }
+        } else {
+            i32x4_t r[C::LOADS];
+            for (int t = 0; t < nb; ++t) {  // load -> barrier -> compute -> barrier
+                load_block(p, slice, t, cp, r);
+                wait_vmcnt<0>();
+                store_block(smem, wave, lane, r);
+                wait_lgkmcnt0();
+                barrier();
+                block(p, smem, L, qf, o, mrun, lrun, t, lane, [] {});
+                barrier();
+            }
+        }
+
+        // O = acc / l for the rows this wave owns inside Sq
+#pragma unroll
+        for (int m = 0; m < C::FM; ++m) {
+            const float inv = 1.0f / xsum(lrun[m]);
+            const int q = qw + 16 * m + i;
+            if (q < p.Sq) {
+                char* row = p.O + ((long long)slice * p.Sq + q) * (C::D * 4);
+#pragma unroll
+                for (int n = 0; n < C::DN; ++n) *(acc_t*)(row + (16 * n + 4 * g) * 4) = o[m][n] * inv;
+            }
+        }
+    }
+};
+
+template <class C>
+__global__ __attribute__((amdgpu_flat_work_group_size(C::THREADS, C::THREADS), amdgpu_waves_per_eu(1, 1))) void
+attention_kernel(AttnArgs p)
+{
+    Attn<C>::run(p);
+}
+
+template <class C>
+static hipError_t launch_attn(const AttnArgs& a, unsigned grid, hipStream_t stream)
+{
+    AttnArgs arg = a;
+    arg.kv_blocks = (a.Sk + C::BKV - 1) / C::BKV;
+    void* args[] = {&arg};
+    return hipLaunchKernel((const void*)&attention_kernel<C>, dim3(grid), dim3(C::THREADS), args, 0, stream);
+}
+
+typedef hipError_t (*AttnLaunch)(const AttnArgs&, unsigned, hipStream_t);
+
+template <int DT, int D>
+static AttnLaunch pick(int variant, int stages)
+{
+    if (variant == V_SYNC) return &launch_attn<AttnCfg<DT, D, V_SYNC, 1>>;
+    if (variant == V_REG) return stages == 1 ? &launch_attn<AttnCfg<DT, D, V_REG, 1>> : &launch_attn<AttnCfg<DT, D, V_REG, 2>>;
+    return stages == 2 ? &launch_attn<AttnCfg<DT, D, V_DIRECT, 2>> : &launch_attn<AttnCfg<DT, D, V_DIRECT, 3>>;
+}
+
+hipError_t launch_attention(int dtype, int D, int variant, int stages, const void* Q, const void* K, const void* V,
+                            void* O, int BH, int Sq, int Sk, float c, hipStream_t stream)
+{
+    AttnArgs a;
+    a.Q = (const char*)Q;
+    a.K = (const char*)K;
+    a.V = (const char*)V;
+    a.O = (char*)O;
+    a.BH = BH;
+    a.Sq = Sq;
+    a.Sk = Sk;
+    a.q_blocks = (Sq + 255) / 256;
+    a.c = c;
+    AttnLaunch f = dtype == DT_F16 ? (D == 64 ? pick<DT_F16, 64>(variant, stages) : pick<DT_F16, 128>(variant, stages))
+                                   : (D == 64 ? pick<DT_BF16, 64>(variant, stages) : pick<DT_BF16, 128>(variant, stages));
+    return f(a, (unsigned)(BH * a.q_blocks), stream);
+}
+
+}  // namespace spt

@@ -36,6 +36,11 @@ KernelTable kernels_f32_col();
 // The streaming pipeline y = 2 x (spt_stream.hip); arguments already validated.
 hipError_t launch_scale_by_two(const void* x, void* y, int64_t n, int stages, unsigned blocks, hipStream_t stream);
 
+// The attention-style consumer (spt_attention.hip); arguments already validated.
+// c = scale * log2(e).
+hipError_t launch_attention(int dtype, int D, int variant, int stages, const void* Q, const void* K, const void* V,
+                            void* O, int BH, int Sq, int Sk, float c, hipStream_t stream);
+
 // nullptr when that combination is not built.  exact = 1 asks for the
 // instantiation that assumes M, N, K are multiples of the tile.
 const KernelEntry* find_kernel(int dtype, int bcol, int tile, int variant, int stages, int exact, int window = 0);

@@ -37,6 +37,11 @@ SPT_EMPTY_TABLE(i8_col)
 SPT_EMPTY_TABLE(f32_row)
 SPT_EMPTY_TABLE(f32_col)
 hipError_t launch_scale_by_two(const void*, void*, int64_t, int, unsigned, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_attention(int, int, int, int, const void*, const void*, const void*, void*, int, int, int, float,
+                            hipStream_t)
+{
+    return hipErrorInvalidValue;
+}
 }  // namespace spt
 
 static uint64_t state = 0x9E3779B97F4A7C15ull;
@@ -121,6 +126,12 @@ int main()
         rc = spt_scale_by_two(M, A, C, stages, variant, nullptr);
         expect(known(rc), "spt_scale_by_two status", rc);
         expect(rc != SPT_OK || M == 0, "OK with work to launch", rc);
+        message_ok(rc);
+
+        rc = spt_attention(M, N, K, (int64_t)((unsigned)stages % 5) * 32, A, B, (const void*)((uintptr_t)B + 4096), C,
+                           (float)(int)(next() % 3) - 0.5f, dtype, nullptr, variant, stages);
+        expect(known(rc), "spt_attention status", rc);
+        expect(rc != SPT_OK || M == 0 || N == 0, "OK with work to launch", rc);
         message_ok(rc);
 
         expect(spt_status_string(rc) != nullptr && spt_status_string(layout) != nullptr, "status string", rc);

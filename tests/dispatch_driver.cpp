@@ -62,6 +62,11 @@ SPT_RECORDING_TABLE(i8_col, DT_I8, 1)
 SPT_RECORDING_TABLE(f32_row, DT_F32, 0)
 SPT_RECORDING_TABLE(f32_col, DT_F32, 1)
 hipError_t launch_scale_by_two(const void*, void*, int64_t, int, unsigned, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_attention(int, int, int, int, const void*, const void*, const void*, void*, int, int, int, float,
+                            hipStream_t)
+{
+    return hipErrorInvalidValue;
+}
 }  // namespace spt
 
 int main()

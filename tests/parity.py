@@ -80,3 +80,31 @@ def sample_entries(M: int, N: int, n: int, rng: np.random.Generator, BM: int = 1
             r.append(i)
             c.append(j)
     return np.array(r, dtype=np.int64), np.array(c, dtype=np.int64)
+
+
+# Attention: O_gpu - O_ref at (b, i, d), over max_j |V[b, j, d]|.  The softmax weights of a
+# row sum to one, so |O[b, i, d]| <= max_j |V[b, j, d]|: this is the scale of every output
+# in column d.  Rounding the probabilities to the input type before the second product
+# perturbs each by at most 2^-8 (bf16) or 2^-11 (fp16) relatively, hence the output by
+# at most that times max_j |V[b, j, d]|; fp32 sums add far less.
+TOL_ATTN = {"f16": 2e-3, "bf16": 8e-3}
+
+
+def attention_error(o_gpu, o_ref, v_bits, dtype) -> float:
+    v = values(np.ascontiguousarray(v_bits), dtype)           # (BH, Sk, D)
+    scale = np.max(np.abs(v), axis=1, keepdims=True)           # (BH, 1, D)
+    if not np.all(np.isfinite(o_gpu)):
+        return float("inf")
+    err = np.abs(o_gpu.astype(np.float64) - o_ref)
+    zero = scale == 0
+    if np.any(np.broadcast_to(zero, err.shape) & (o_gpu != 0)):
+        return float("inf")
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(zero, 0.0, err / np.where(zero, 1.0, scale))
+    return float(r.max()) if r.size else 0.0
+
+
+def check_attention(o_gpu, o_ref, v_bits, dtype) -> float:
+    e = attention_error(o_gpu, o_ref, v_bits, dtype)
+    assert e <= TOL_ATTN[dtype], f"attention normalised error {e:.3e} > {TOL_ATTN[dtype]:.1e}"
+    return e

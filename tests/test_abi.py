@@ -28,7 +28,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert names == sorted(["spt_gemm", "spt_gemm_ex", "spt_plan", "spt_status_string",
-                            "spt_last_error", "spt_version", "spt_scale_by_two"])
+                            "spt_last_error", "spt_version", "spt_scale_by_two", "spt_attention"])
     for n in names:
         assert hasattr(L, n), n
 
