@@ -195,6 +195,13 @@ typedef struct spt_plan_info {
     int32_t band_stages;
     int64_t band_m;
     int64_t band_grid;
+    /* 1: the DIRECT ring copies the partial last K tile itself, zero-filled past K
+       per 16-byte chunk ("Hiding Memory Latency ...", section 8: a partial tile's
+       copy fills what lies outside the source with zeros); this needs k_tail * elt
+       to be a multiple of 16 and a tile other than the 256 x 256 ones.  0: a
+       partial tile (if any) is loaded through VGPRs with every element past K
+       zeroed, after the ring. */
+    int32_t tail_ring;
 } spt_plan_info;
 
 /* C = A*B with B row-major, the library's choice of tile and variant. */

@@ -197,6 +197,15 @@ static void plan_band(int64_t M, int64_t N, int64_t K, spt_plan_info& p)
     p.grid = rows_main * p.tiles_n;
 }
 
+// The DIRECT ring copies a partial last K tile itself when its k_tail elements
+// are whole 16-byte chunks (each chunk then lies wholly below K or wholly past
+// it, and the copies past K are pointed outside the buffer so they read zeros);
+// else the general kernels load that tile through VGPRs with per-byte masks.
+static int tail_in_ring(int variant, int tile, int k_tail, int elt)
+{
+    return variant == V_DIRECT && ring_tail_tile(tile) && k_tail > 0 && (k_tail * elt) % 16 == 0 ? 1 : 0;
+}
+
 // Checks every argument except the pointers; fills `pi` on success.
 static int make_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, int variant,
                      int stages, int tile, spt_plan_info* pi)
@@ -251,6 +260,7 @@ static int make_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, i
     }
     p.band_m = M;
     p.k_tail = (int32_t)(K - p.k_full_tiles * p.BK);
+    p.tail_ring = tail_in_ring(variant, tile, p.k_tail, elt);
     // "Pipeline GPU Kernel", Schritt 1: smem_a = BM*BK*sizeof(T), smem_b = BK*BN*sizeof(T).
     p.a_stage_bytes = p.BM * p.BK * elt;
     p.b_stage_bytes = p.BK * p.BN * elt;
@@ -386,6 +396,7 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     a.tiles_n = (int)pi.tiles_n;
     a.k_full = (int)pi.k_full_tiles;
     a.k_tail = pi.k_tail;
+    a.tail_ring = pi.tail_ring;
     hipError_t err = e->launch(a, (unsigned)grid, (hipStream_t)stream);
     if (err != hipSuccess) return fail(SPT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(err));
     if (band) {  // rows [M_main, M) on the band tile, after the main grid in stream order
@@ -397,6 +408,7 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
         b.tiles_n = (int)((N + TB.BN - 1) / TB.BN);
         b.k_full = (int)(K / (TB.BKB / elt));
         b.k_tail = (int)(K - (int64_t)b.k_full * (TB.BKB / elt));
+        b.tail_ring = tail_in_ring(V_DIRECT, kBandTile, b.k_tail, elt);
         if ((int64_t)b.tiles_m * b.tiles_n != pi.band_grid)
             return fail(SPT_ERR_LAUNCH, "internal: band grid mismatch");
         err = eb->launch(b, (unsigned)pi.band_grid, (hipStream_t)stream);

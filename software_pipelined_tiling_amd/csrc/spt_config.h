@@ -31,6 +31,12 @@ constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 constexpr int elt_bytes(int dt) { return dt == DT_I8 ? 1 : dt == DT_F32 ? 4 : 2; }
 
+// Tiles whose general DIRECT kernels copy a chunk-aligned partial K tile through the
+// ring (GemmArgs::tail_ring).  The 256 x 256 tiles with 128 x 64 and 128 x 128 wave
+// tiles keep the VGPR tail: the in-ring tail costs them registers they do not have
+// (the 8-wave form would spill).
+constexpr bool ring_tail_tile(int tile) { return tile != 2 && tile != 4; }
+
 // gfx950 (CDNA4) per-CU resources (AMD public specification).
 constexpr int kLdsPerCu = 163840;   // 160 KiB
 constexpr int kSimdsPerCu = 4;
@@ -49,6 +55,8 @@ struct GemmArgs {
     int tiles_m, tiles_n;
     int k_full;          // number of full BK-deep tiles
     int k_tail;          // K - k_full * BK (0 = none)
+    int tail_ring;       // 1: the partial tile goes through the DIRECT ring as tile k_full
+                         // (k_tail * elt a multiple of 16: whole chunks are in or past K)
 };
 
 }  // namespace spt

@@ -118,6 +118,7 @@ struct Cfg {
     static constexpr bool EXACT = EXACT_;
     static constexpr bool BLANE = BLANE_ || elt_bytes(DT_) == 4;
     static constexpr int TILE = TILE_, V = V_, S = S_;
+    static constexpr bool RING_TAIL = V_ == V_DIRECT && !EXACT_ && ring_tail_tile(TILE_);  // see GemmArgs::tail_ring
     static constexpr int BM = kTiles[TILE_].BM, BN = kTiles[TILE_].BN;
     static constexpr int ELT = elt_bytes(DT_);
     static constexpr int CE = 16 / ELT;           // elements per 16-byte chunk
@@ -439,6 +440,31 @@ struct Gemm {
         }
     }
 
+    // The partial K tile through the ring (p.tail_ring): before its copies are issued,
+    // every copy whose 16-byte chunk lies at k >= k_tail gets an offset past any
+    // buffer extent, so it reads zeros ("Hiding Memory Latency ...", section 8: the
+    // copy of a partial tile zero-fills what lies outside the source).  Row-major B
+    // needs nothing here: its copies of that tile end after k_tail rows (tail_b).
+    // The ring copies nothing after that tile, so the offsets stay changed.
+    static constexpr int OFF_PAST = (int)0xfffff000u;  // + at most 3 KiB of immediate: past every extent
+    static __device__ void mask_tail(const GemmArgs& p, int tid, Copy& cp)
+    {
+#pragma unroll
+        for (int i = 0; i < C::A_CPT; ++i) {
+            int r, k;
+            a_src(chunk_of(i, tid, C::A_CPT), r, k);
+            if (k >= p.k_tail) cp.a_voff[i] = OFF_PAST;
+        }
+        if constexpr (C::BCOL) {
+#pragma unroll
+            for (int i = 0; i < C::B_CPT; ++i) {
+                int k, n;
+                b_src(chunk_of(i, tid, C::B_CPT), k, n);
+                if (k >= p.k_tail) cp.b_voff[i] = OFF_PAST;
+            }
+        }
+    }
+
     // Tile bases and readable byte counts for K tile t (wave-uniform values).
     // The count covers exactly what the caller guarantees readable from the
     // base: whole row pitches of the rows this tile touches.
@@ -477,8 +503,9 @@ struct Gemm {
         i32x4_t qa, qb;    // descriptors of the next K tile to copy: base - DMA_BIAS, extent
         uint64_t sa, sb;   // bytes between consecutive K tiles
         uint32_t na, nb;   // extent (with DMA_BIAS) of a full K tile
-        int left;          // full K tiles not yet copied
+        int left;          // K tiles not yet copied (the in-ring partial tile included)
         uint32_t m0a, m0b; // LDS byte address of this wave's first A / B block in stage 0
+        uint32_t tail_b;   // extent of the partial tile's row-major B copies (else nb)
     };
     static __device__ __forceinline__ i32x4_t desc(uint64_t base, uint32_t bytes)
     {
@@ -507,9 +534,15 @@ struct Gemm {
             r.sb = (uint64_t)C::BK * p.ldb * C::ELT;
             r.nb = (uint32_t)(((long long)C::BK * p.ldb - n0) * C::ELT) + DMA_BIAS;
         }
-        r.left = p.k_full;
+        const int tail = C::RING_TAIL ? p.tail_ring : 0;
+        r.left = p.k_full + tail;
+        r.tail_b = r.nb;
+        if constexpr (!C::BCOL && C::RING_TAIL)
+            // the partial tile's copies of row-major B end after its k_tail rows: the
+            // rows past K read as zeros
+            if (tail) r.tail_b = (uint32_t)(((long long)p.k_tail * p.ldb - n0) * C::ELT) + DMA_BIAS;
         r.qa = desc(a, r.left > 0 ? r.na : 0u);
-        r.qb = desc(b, r.left > 0 ? r.nb : 0u);
+        r.qb = desc(b, r.left > 0 ? (r.left == 1 ? r.tail_b : r.nb) : 0u);
         const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
         r.m0a = lds0 + (uint32_t)(wave * C::A_CPT) * 1024u;
         r.m0b = lds0 + (uint32_t)C::A_BYTES + (uint32_t)(wave * C::B_CPT) * 1024u;
@@ -531,7 +564,7 @@ struct Gemm {
         if (part == 2) {
             r.left -= 1;
             r.qa[2] = (int)(r.left > 0 ? r.na : 0u);
-            r.qb[2] = (int)(r.left > 0 ? r.nb : 0u);
+            r.qb[2] = (int)(r.left > 1 ? r.nb : r.left == 1 ? r.tail_b : 0u);
         }
     }
 
@@ -843,16 +876,18 @@ struct Gemm {
     // constant.  The last tile's reads of "tile nf" are discarded; the ring is
     // drained before the kernel leaves.
     static __device__ __forceinline__ void loop_direct(const GemmArgs& p, int m0, int n0, int wave,
-                                                       const Lanes& L, SPT_LDS char* smem, const Copy& cp,
+                                                       const Lanes& L, SPT_LDS char* smem, Copy& cp,
                                                        acc_t (&acc)[C::FM][C::FN])
     {
-        const int nf = p.k_full;
+        const int nf = p.k_full + (C::RING_TAIL ? p.tail_ring : 0);
         if (nf == 0) return;
         Ring r;
         ring_init(p, m0, n0, wave, smem, r);
         // prologue: tiles 0 .. S-1 into stages 0 .. S-1
 #pragma unroll
         for (int i = 0; i < C::S; ++i) {
+            if constexpr (C::RING_TAIL)
+                if (p.tail_ring && i == p.k_full) mask_tail(p, threadIdx.x, cp);
             const Dma d = dma_of(r, i * C::STAGE_BYTES);
             static_for<0, C::LOADS>([&](auto jc) { dma_issue<decltype(jc)::value>(d, cp); });
             ring_advance(r, 0);
@@ -867,15 +902,15 @@ struct Gemm {
         int t = 0;
         uint32_t rs = 0;  // byte offset of the stage tile t sits in
         if constexpr (C::KS % 2 == 0) {
-            for (; t < nf; ++t) tile_direct<0>(r, rs, L, smem, cp, sl, acc);
+            for (; t < nf; ++t) tile_direct<0>(p, r, rs, L, smem, cp, sl, acc);
         } else {
             for (; t + 1 < nf; t += 2) {
-                tile_direct<0>(r, rs, L, smem, cp, sl, acc);
-                tile_direct<1>(r, rs, L, smem, cp, sl, acc);
+                tile_direct<0>(p, r, rs, L, smem, cp, sl, acc);
+                tile_direct<1>(p, r, rs, L, smem, cp, sl, acc);
             }
             // (exact-fit kernels with one k-step per tile are dispatched for an even nf only)
             if constexpr (!C::EXACT)
-                if (t < nf) tile_direct<0>(r, rs, L, smem, cp, sl, acc);
+                if (t < nf) tile_direct<0>(p, r, rs, L, smem, cp, sl, acc);
         }
         wait_vmcnt<0>();  // no copy may still be writing this workgroup's LDS
     }
@@ -883,8 +918,8 @@ struct Gemm {
     // One K tile in the stage at byte offset rs (advanced to the next stage on
     // return); its k-step s uses register slot (P + s) & 1.
     template <int P>
-    static __device__ __forceinline__ void tile_direct(Ring& r, uint32_t& rs, const Lanes& L,
-                                                       const SPT_LDS char* smem, const Copy& cp, Slot (&sl)[2],
+    static __device__ __forceinline__ void tile_direct(const GemmArgs& p, Ring& r, uint32_t& rs, const Lanes& L,
+                                                       const SPT_LDS char* smem, Copy& cp, Slot (&sl)[2],
                                                        acc_t (&acc)[C::FM][C::FN])
     {
         const uint32_t nx = rs + C::STAGE_BYTES == (uint32_t)C::LDS_BYTES ? 0u : rs + C::STAGE_BYTES;
@@ -899,6 +934,8 @@ struct Gemm {
                 wait_lgkmcnt0();                       // this wave's reads of this tile are complete
                 wait_vmcnt<(C::S - 2) * C::LOADS>();   // its copies of the next tile have landed
                 barrier();                             // next tile visible to all; this stage free
+                if constexpr (C::RING_TAIL)
+                    if (r.left == 1 && p.tail_ring) mask_tail(p, threadIdx.x, cp);  // tile + S is the partial one
                 const Dma d = dma_of(r, rs);           // tile + S into this stage
 #ifdef SPT_POISON
                 poison(r, rs);
@@ -974,7 +1011,8 @@ struct Gemm {
             loop_direct(p, m0, n0, wave, L, smem, cp, acc);
         }
 
-        if (!C::EXACT && p.k_tail) {  // partial last tile, zero-filled beyond K, through VGPRs
+        if (!C::EXACT && p.k_tail && !(C::RING_TAIL && p.tail_ring)) {
+            // partial last tile, zero-filled beyond K, through VGPRs
             load_tail(p, m0, n0, tid, ra, rb);
             wait_vmcnt<0>();
             wait_lgkmcnt0();

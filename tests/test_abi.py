@@ -350,3 +350,25 @@ def test_plan_info_mirror_matches_the_c_layout(tmp_path):
     assert int(got["size"]) == ctypes.sizeof(spt.PlanInfo)
     for f in fields:
         assert int(got[f]) == getattr(spt.PlanInfo, f).offset, f
+
+
+@pytest.mark.parametrize("dtype,M,N,K,lay,variant,stages,tile,want", [
+    (spt.BF16, 4000, 3000, 1000, spt.ROW, 0, 0, 0, 1),   # the ragged workload: a 40-wide tail, 80 bytes
+    (spt.BF16, 4000, 3000, 333, spt.ROW, 0, 0, 0, 0),    # 13 elements: not whole chunks
+    (spt.I8, 300, 600, 64 * 5 + 16, spt.COL, 3, 2, 1, 1),
+    (spt.I8, 300, 600, 64 * 5 + 8, spt.COL, 3, 2, 1, 0),
+    (spt.F32, 300, 600, 16 * 4 + 4, spt.ROW, 3, 3, 3, 1),
+    (spt.F16, 300, 600, 40, spt.ROW, 3, 3, 1, 1),        # no full tile: only the partial one
+    (spt.F16, 300, 600, 40, spt.ROW, 1, 1, 1, 0),        # SYNC and REG keep the VGPR tail
+    (spt.F16, 300, 600, 40, spt.ROW, 2, 2, 1, 0),
+    (spt.F16, 600, 600, 72, spt.ROW, 3, 2, 2, 0),        # the 256 x 256 tiles keep it too
+    (spt.F16, 600, 600, 72, spt.ROW, 3, 2, 4, 0),
+    (spt.F16, 600, 600, 72, spt.ROW, 3, 2, 6, 1),
+    (spt.F16, 512, 512, 512, spt.ROW, 3, 2, 1, 0),       # no partial tile
+])
+def test_tail_ring_plan(L, dtype, M, N, K, lay, variant, stages, tile, want):
+    rc, pi = spt.spt_plan(dtype, M, N, K, lay, variant, stages, tile)
+    assert rc == 0, spt.spt_last_error()
+    assert pi.tail_ring == want
+    if want:
+        assert (pi.k_tail * pi.elt_bytes) % 16 == 0 and pi.k_tail > 0

@@ -160,6 +160,37 @@ def test_variants_bit_identical_ragged(oracle_mod, dtype, b_col, tile):
         assert np.array_equal(C.view(np.uint32), outs[0].view(np.uint32))
 
 
+RING_TAIL_TILES = {1: (2, 3, 4), 3: (2, 3, 4), 5: (2, 3, 4), 6: (2,)}  # DIRECT rings built per tile
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8", "f32"])
+@pytest.mark.parametrize("b_col", [False, True])
+@pytest.mark.parametrize("tile", sorted(RING_TAIL_TILES))
+def test_partial_tile_through_the_ring(oracle_mod, dtype, b_col, tile):
+    """K tails of whole 16-byte chunks go through the DIRECT ring itself, zero-filled
+    past K per chunk ("Hiding Memory Latency ...", section 8): with no full tile
+    before them, inside the prologue, and after the steady state; NaN padding past K
+    must not leak.  Every ring depth agrees with the oracle and bit for bit with the
+    unpipelined loop, whose tail goes through VGPRs."""
+    e = I.ELT_BYTES[dtype]
+    BK = (128 if tile == 6 else 64) // e
+    ch = 16 // e
+    BM, BN = {1: (128, 256), 3: (128, 128), 5: (256, 256), 6: (256, 192)}[tile]
+    M, N = BM + 37, BN + 20
+    for K in (ch, BK + ch, 2 * BK + 3 * ch, 4 * BK + BK - ch, 9 * BK + 2 * ch):
+        A, B = operands(dtype, b_col, M, N, K, 17 + K, lda_pad=8, ldb_pad=8)
+        Cref = ref(oracle_mod, A, B, dtype, b_col, N, K)
+        C1 = run(A, B, dtype, b_col, M, N, K, "sync", 1, tile)
+        parity.check_full(C1, Cref, A, B, dtype, b_col, M, N, K)
+        for st in RING_TAIL_TILES[tile]:
+            rc, pi = spt.spt_plan(spt.DTYPE_CODES[dtype], M, N, K, spt.COL if b_col else spt.ROW,
+                                  spt.VARIANT_DIRECT, st, tile)
+            assert rc == 0 and pi.tail_ring == 1 and pi.k_tail > 0
+            C = run(A, B, dtype, b_col, M, N, K, "direct", st, tile)
+            parity.check_full(C, Cref, A, B, dtype, b_col, M, N, K)
+            assert np.array_equal(C.view(np.uint32), C1.view(np.uint32)), (tile, st, K)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
 def test_integer_valued_bit_exact(oracle_mod, dtype):
     """Integer inputs (|a|,|b| <= 4; int8 full range): every partial sum is exact in the
