@@ -256,9 +256,18 @@ struct Gemm {
     // c of k-row r at c ^ swz_n(r); read by ds_read_b64_tr_b16 / tr_b8.
     static constexpr int RN = C::BN * C::ELT, NCN = RN / 16;
     // The XOR permutes chunks within groups of SWG: 8, or 4 for int8 k-rows of 12
-    // chunks (the 192-column tile), which hold no whole group of 8.
-    static constexpr int SWG = (C::ELT == 1 && NCN % 8 != 0) ? 4 : 8;
-    static __device__ __forceinline__ constexpr int swz_n(int r) { return C::ELT == 2 ? ((r & 3) << 1) : (r & (SWG - 1)); }
+    // chunks (the 192-column tile), which hold no whole group of 8.  16-bit k-rows
+    // of a whole number of 256-byte bank lines (16 chunks) XOR the chunk pair with
+    // k-row bits 0, 1 and 3: the 8 k-rows one half-wave of a transposing read
+    // touches (8g + 0..3 for g = 0, 1; 16 + 8g' + 0..3) then sit in 8 different
+    // 32-byte bank groups.  With bits 0 and 1 alone, k-rows r and r + 8 shared
+    // their banks: two conflict cycles per read (SQ_LDS_BANK_CONFLICT on MI355X).
+    static constexpr bool WIDE16 = C::ELT == 2 && NCN % 16 == 0;
+    static constexpr int SWG = WIDE16 ? 16 : (C::ELT == 1 && NCN % 8 != 0) ? 4 : 8;
+    static __device__ __forceinline__ constexpr int swz_n(int r)
+    {
+        return WIDE16 ? (((r & 3) | ((r >> 1) & 4)) << 1) : C::ELT == 2 ? ((r & 3) << 1) : (r & (SWG - 1));
+    }
     static_assert(C::BCOL || C::BLANE || NCN % SWG == 0, "the k-row swizzle permutes chunks within groups");
     // Row-major B, lane layout: block (nb, s, h) of 64 lanes x (8 | 8 | 4) bytes
     // in the order of the lanes of one ds_read_b64_tr_b16 / tr_b8 / ds_read_b32.
@@ -322,10 +331,10 @@ struct Gemm {
     // MFMA row 0 / column 0 of the wave tile; other rows / columns add an
     // immediate.  A fragment (m, s): 16 rows x the 16-byte chunk 4s + g.
     // Row layout: the swizzle only permutes column blocks within groups of BQ
-    // (4 for tr_b16, 8 for tr_b8; the wave's first block is a multiple of BQ),
-    // so blocks n and n + BQ sit 128 bytes apart in every k-row and one lane
-    // offset per n mod BQ serves all FN blocks.
-    static constexpr int BQ_ = C::ELT == 2 ? 4 : 8;
+    // (4 for tr_b16, 8 for tr_b16 on 16-chunk groups and for tr_b8; the wave's
+    // first block is a multiple of BQ), so blocks n and n + BQ sit BQ blocks
+    // apart in every k-row and one lane offset per n mod BQ serves all FN blocks.
+    static constexpr int BQ_ = C::ELT == 2 && !WIDE16 ? 4 : 8;
     static constexpr int BQ = C::FN % BQ_ == 0 ? BQ_ : C::FN;
     static constexpr int B_OFFS = C::BCOL ? C::KS : (C::BLANE ? 1 : BQ);
     struct Lanes {
@@ -345,7 +354,8 @@ struct Gemm {
             L.b[0] = br_block(nb0, 0, 0) + lane * (C::ELT == 4 ? 4 : 8);
         } else if constexpr (!C::BCOL && C::ELT == 2) {
             // tr_b16: lane (g, i) fetches k-row 8g + (i >> 2) (+ 4h + KSTEP s) at columns
-            // 4 (i & 3) .. + 3 of column block nb; swz_n only sees k-row bits 0, 1.
+            // 4 (i & 3) .. + 3 of column block nb; swz_n only sees k-row bits 0, 1 and 3,
+            // which 4h + KSTEP s never change.
 #pragma unroll
             for (int n = 0; n < BQ; ++n) {
                 const int kr = 8 * g + (l16 >> 2);
@@ -383,7 +393,7 @@ struct Gemm {
                 o0 = L.b[0] + (br_block(n, s, 0) - C::A_BYTES);
                 o1 = L.b[0] + (br_block(n, s, 1) - C::A_BYTES);
             } else {
-                o0 = L.b[n % BQ] + (n / BQ) * 128 + s * C::KSTEP * RN;
+                o0 = L.b[n % BQ] + (n / BQ) * (BQ * 16 * C::ELT) + s * C::KSTEP * RN;
                 o1 = o0 + (C::ELT == 2 ? 4 : 8) * RN;
             }
             if constexpr (C::ELT == 2) {
