@@ -509,6 +509,8 @@ def main():
     ap.add_argument("--only-headline", action="store_true", help="headline workload only (profiling)")
     ap.add_argument("--only-workload", default=None,
                     help="time only this side workload by name prefix, e.g. 'bf16 GEMM 8192' (profiling)")
+    ap.add_argument("--only-attention", action="store_true",
+                    help="besides the headline, time only the attention leg (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain 256 MiB device copies (HBM counter scale)")
     args = ap.parse_args()
@@ -609,7 +611,7 @@ def main():
                                        "value_over_vendor": round(vu / (ms * 1e3), 3),
                                        "what": "torch.mm(A, B, out_dtype=float32) on the same operands (context)"}
 
-    if args.only_workload:
+    if args.only_workload or args.only_attention:
         args.no_sweep = True
     if not args.only_headline:
         steps = max(20, min(args.steps, 100))
@@ -639,7 +641,7 @@ def main():
         del head
         extra = {}
         for wk in [I.W_I8_4096, I.W_BF16_RAGGED, I.W_F16_256] + [I.w_bf16_lowk(k) for k in I.LOWK_KS]:
-            if args.only_workload and not wk.name.startswith(args.only_workload):
+            if (args.only_workload and not wk.name.startswith(args.only_workload)) or args.only_attention:
                 continue
             p = Problem(wk)
             us, us1 = gemm_us(p), gemm_us(p, "sync", 1)
@@ -674,8 +676,9 @@ def main():
         out["workloads_timing"] = ("every side workload: 20 calls captured in one HIP graph, replayed 10 times "
                                    "between two events after one untimed replay (GPU time of back-to-back calls)")
 
-        if not args.only_workload:
+        if not args.only_workload and not args.only_attention:
             out["streaming"] = stream_bench(steps, 20)
+        if not args.only_workload:
             out["attention"] = attention_bench()
 
     if not args.no_cpu_baseline:

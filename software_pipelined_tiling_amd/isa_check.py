@@ -35,6 +35,11 @@ counts.  `check(kernel)` turns that into pass/fail properties:
   unpipelined reference).  REG: the tile's global loads are issued before the
   first MFMA of the iteration and their vmcnt wait comes after the last one.
 
+The attention consumer's kernels are checked too (`check_attention`): per
+key block the MFMAs of both products, DIRECT's copies, barrier and one
+vmcnt((S-2) x copies) wait, REG's loads before the block's last MFMA and its
+vmcnt(0) after it, SYNC's vmcnt(0) before its first MFMA, no scratch.
+
 The streaming kernel (y = 2x, "Hiding Memory Latency ...", section 8) is
 checked too (`check_stream`): per loop iteration one copy, one store and one
 barrier, and the steady wait vmcnt(2S-3) (S >= 2: copies and stores share
@@ -288,6 +293,78 @@ def check_stream(k: StreamKernel) -> Dict[str, bool]:
            "vmcnt": vm == ([0] if S == 1 else [2 * S - 3]),
            "lds": k.meta.get("lds") == S * 4096,
            "clean": not any(x.startswith("scratch_") for x in body)}
+    return res
+
+
+@dataclasses.dataclass
+class AttnKernel:
+    name: str
+    dtype: int
+    D: int
+    variant: str
+    stages: int
+    instrs: List[str]
+    meta: Dict[str, int]
+
+    @property
+    def geometry(self):
+        """Per key block: BKV keys, MFMAs per wave (S = Q K^T, then O += P V over the
+        wave's 64 query rows), 16-byte copies per thread, stage bytes (K and V blocks)."""
+        bkv = 32 if self.D == 128 else 64
+        mfma = 4 * (bkv // 16) * (self.D // 32) + 4 * (self.D // 16) * (bkv // 32)
+        loads = 2 * (bkv * self.D * 2) // 16 // 256
+        return dict(bkv=bkv, mfma_per_block=mfma, loads_per_block=loads, stage_bytes=2 * bkv * self.D * 2)
+
+
+_ATTN = re.compile(r"AttnCfgILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E")
+
+
+def load_attention(lib: Optional[str] = None) -> List[AttnKernel]:
+    """The attention consumer's kernels (csrc/spt_attention.hip)."""
+    lib = lib or os.path.join(HERE, "libspt.so")
+    out: List[AttnKernel] = []
+    for co in code_objects(lib):
+        meta = _metadata(co)
+        for name, instrs in _disassemble(co).items():
+            m = _ATTN.search(name)
+            if m and "attention_kernel" in name:
+                dt, d, v, s = (int(x) for x in m.groups())
+                out.append(AttnKernel(name, dt, d, VARIANTS[v], s, instrs, meta.get(name, {})))
+    return out
+
+
+def check_attention(k: AttnKernel) -> Dict[str, bool]:
+    """The key/value block loop of an attention kernel (the loop body holding the
+    most MFMAs): one block's MFMAs; DIRECT: its copies, one barrier and one vmcnt
+    wait of (S-2) x copies, so the copies of the S-2 younger blocks stay in flight;
+    REG: the block's global loads issued before the last MFMA and one vmcnt(0)
+    after it; SYNC: vmcnt(0) before the first MFMA; no scratch anywhere; the LDS
+    ring of S stages."""
+    g = k.geometry
+    body = steady_loop(k)
+    L, S = g["loads_per_block"], k.stages
+    loads = [i for i, x in enumerate(body) if x.startswith("buffer_load") and not x.rstrip().endswith("lds")]
+    if loads:  # read the loop as a cycle starting at its first global load
+        body = body[loads[0]:] + body[:loads[0]]
+        loads = [i for i, x in enumerate(body) if x.startswith("buffer_load") and not x.rstrip().endswith("lds")]
+    mf = [i for i, x in enumerate(body) if x.startswith("v_mfma")]
+    vm = [(i, int(m.group(1))) for i, x in enumerate(body) for m in [re.search(r"vmcnt\((\d+)\)", x)] if m]
+    bar = sum(x.startswith("s_barrier") for x in body)
+    res = {"counts": _count_mfma(body) == g["mfma_per_block"],
+           "clean": k.meta.get("scratch") == 0 and not any(x.startswith("scratch_") for x in body),
+           "lds": k.meta.get("lds") == S * g["stage_bytes"]}
+    if k.variant == "direct":
+        res["copies"] = _count_copies(body) == L and bar == 1
+        res["vmcnt"] = [v for _, v in vm] == [(S - 2) * L]
+    elif k.variant == "reg":
+        # from the loads on: MFMAs before the first wait, which is vmcnt(0) (the compiler adds its
+        # own, already satisfied, partial waits before each staged ds_write)
+        res["copies"] = len(loads) == L and bar == (2 if S == 1 else 1)
+        res["vmcnt"] = bool(mf) and bool(vm) and vm[0][1] == 0 and mf[0] < vm[0][0]
+    else:
+        # from the loads on: vmcnt(0) before any MFMA
+        res["copies"] = len(loads) == L and bar == 2
+        res["vmcnt"] = bool(mf) and bool(vm) and vm[0][1] == 0 and vm[0][0] < mf[0]
     return res
 
 

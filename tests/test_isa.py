@@ -123,6 +123,20 @@ def test_streaming_ring_schedule(built_lib):
         assert all(res.values()), (k.name, res)
 
 
+def test_attention_schedule(built_lib):
+    """The attention consumer (both element types, head dimension 64 and 128, every
+    producer): per key block the MFMAs of both products; DIRECT's copies, one barrier
+    and one vmcnt((S-2) x copies) wait; REG's loads overlapped with MFMAs before their
+    vmcnt(0); SYNC's vmcnt(0) before any MFMA; no scratch; the LDS ring of S stages."""
+    ks = X.load_attention()
+    assert sorted({(k.dtype, k.D, k.variant, k.stages) for k in ks}) == sorted(
+        (dt, d, v, s) for dt in (0, 1) for d in (64, 128)
+        for v, s in (("sync", 1), ("reg", 1), ("reg", 2), ("direct", 2), ("direct", 3)))
+    for k in ks:
+        res = X.check_attention(k)
+        assert all(res.values()), (k.name, res)
+
+
 def test_persistent_ring_schedule(built_lib):
     """The persistent kernels (128 x 128 tile, windows of 2, 4 and 8 K tiles): per
     K tile of the steady loop the MFMAs, copies and barrier of the ring plus
@@ -186,6 +200,45 @@ def test_checks_catch_planted_schedule_faults(kernels, tile, stages):
     for name, (edits, prop) in planted.items():
         res = X.check(_planted(k, edits))
         assert not res[prop], (name, res)
+
+
+def test_attention_checks_catch_planted_faults(built_lib):
+    """Faults planted in copies of the shipped attention kernels (CPU only): DIRECT
+    with its steady vmcnt wait removed, loosened or (3 stages) made a full drain,
+    or a copy dropped; SYNC with its vmcnt(0) moved after the block's first MFMA;
+    REG with its vmcnt(0) moved before the MFMAs that should overlap the loads."""
+    ks = {(k.dtype, k.D, k.variant, k.stages): k for k in X.load_attention()}
+    for st in (2, 3):
+        k = ks[(0, 128, "direct", st)]
+        assert all(X.check_attention(k).values())
+        ops = _ops(k)
+        body_start = ops.index(X.steady_loop(k)[0])
+        vm = next(i for i in range(body_start, len(ops)) if re.search(r"vmcnt\(\d+\)", ops[i]))
+        want = int(re.search(r"vmcnt\((\d+)\)", ops[vm]).group(1))
+        dma = next(i for i in range(vm, len(ops)) if _is_dma(ops[i]))
+        planted = {"no wait": [(vm, "s_nop 0")], "wait too loose": [(vm, f"s_waitcnt vmcnt({want + 1})")],
+                   "copy dropped": [(dma, "s_nop 0")]}
+        if want:
+            planted["early wait"] = [(vm, "s_waitcnt vmcnt(0)")]
+        for name, edits in planted.items():
+            res = X.check_attention(_planted(k, edits))
+            assert not all(res.values()), (st, name, res)
+    for v, st in (("sync", 1), ("reg", 2)):
+        k = ks[(0, 128, v, st)]
+        assert all(X.check_attention(k).values())
+        ops = _ops(k)
+        loop = X.steady_loop(k)
+        start = ops.index(loop[0])
+        idx = range(start, start + len(loop))
+        first_load = next(i for i in idx if ops[i].startswith("buffer_load"))
+        wait = next(i for i in idx if i > first_load and re.search(r"vmcnt\(0\)", ops[i]))
+        mfma_after = next(i for i in idx if i > first_load and ops[i].startswith("v_mfma"))
+        if v == "sync":  # swap the drain with the first MFMA after the loads: compute overlaps them
+            i, j = wait, next(i for i in idx if i > wait and ops[i].startswith("v_mfma"))
+        else:  # move the drain up to right after the loads, before the MFMAs that overlap them
+            i, j = wait, next(i for i in idx if i > max(x for x in idx if ops[x].startswith("buffer_load")))
+        res = X.check_attention(_planted(k, [(i, ops[j]), (j, ops[i])]))
+        assert not res["vmcnt"], (v, res, mfma_after)
 
 
 # The kernels the library's own choice runs, and the exact-fit forms that the pipelining
