@@ -172,6 +172,25 @@ struct Attn {
         });
     }
 
+#ifdef SPT_POISON
+    // Race-detection builds only (never in the shipped library): before the copies of
+    // a block are issued into a stage, this wave fills the 1 KiB blocks they will
+    // refill with NaN and waits for those writes.  A read of the stage before its
+    // copies land then turns the output into NaN.
+    static __device__ __forceinline__ void poison(uint32_t st, int wave, int lane)
+    {
+        constexpr int pv = C::DT == DT_F16 ? 0x7E007E00 : 0x7FC07FC0;
+        const i32x4_t v = {pv, pv, pv, pv};
+#pragma unroll
+        for (int j = 0; j < C::CPW; ++j) {
+            const uint32_t o = st + (uint32_t)((wave * C::CPW + j) * 1024 + 16 * lane);
+            *(SPT_LDS i32x4_t*)(size_t)o = v;
+            *(SPT_LDS i32x4_t*)(size_t)(o + C::KV_BYTES) = v;
+        }
+        wait_lgkmcnt0();
+    }
+#endif
+
     // REG / SYNC: the same chunks through VGPRs.
     static __device__ __forceinline__ void load_block(const AttnArgs& p, int slice, int t, const Copy& cp,
                                                       i32x4_t (&r)[C::LOADS])
@@ -434,6 +453,9 @@ struct Attn {
 #pragma unroll
             for (int b = 0; b < C::S - 1; ++b) {
                 block_desc(p, slice, b, dk, dv);
+#ifdef SPT_POISON
+                poison(lds0 + b * C::STAGE_BYTES, wave, lane);
+#endif
                 dma_block(cp, dk, dv, lds0 + b * C::STAGE_BYTES, wave);
             }
             uint32_t rs = 0;                                   // stage of block t
@@ -443,6 +465,9 @@ struct Attn {
                 wait_vmcnt<(C::S - 2) * C::LOADS>();          // its copies of block t have landed
                 barrier();                                    // block t visible; the stage of t-1 free
                 block_desc(p, slice, t + C::S - 1, dk, dv);
+#ifdef SPT_POISON
+                poison(lds0 + ws, wave, lane);
+#endif
                 dma_block(cp, dk, dv, lds0 + ws, wave);       // block t+S-1 into that stage
                 block(p, smem + rs, L, qf, o, mrun, lrun, t, lane, [] {});
                 rs = rs + C::STAGE_BYTES == (uint32_t)C::LDS_BYTES ? 0u : rs + C::STAGE_BYTES;
