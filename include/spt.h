@@ -202,6 +202,14 @@ typedef struct spt_plan_info {
        partial tile (if any) is loaded through VGPRs with every element past K
        zeroed, after the ring. */
     int32_t tail_ring;
+    /* DIRECT rings whose S full stages exceed the 160 KiB of LDS, on a tile whose A and
+       B parts are the same size (S = 3 on the 256 x 256 x 128-byte tiles): 2S - 1, the
+       ring runs as that many half-stage slots, each holding the A or the B part of one
+       K tile, and lds_bytes = (2S - 1) * a_stage_bytes.  Copies of the half stage after
+       the next K tile stay in flight at each wait (steady_vmcnt), where a 2-stage ring
+       drains them ("Hiding Memory Latency ...", section 6: deeper pipelines keep more
+       copies in flight).  0 otherwise. */
+    int32_t half_stage_slots;
 } spt_plan_info;
 
 /* C = A*B with B row-major, the library's choice of tile and variant. */

@@ -55,7 +55,7 @@ class PlanInfo(ctypes.Structure):
         ("ratio_flop_per_byte", ctypes.c_double), ("ratio_mfma_per_load", ctypes.c_double),
         ("store_window", ctypes.c_int32), ("tiles_per_wg", ctypes.c_int32),
         ("band_tile", ctypes.c_int32), ("band_stages", ctypes.c_int32), ("band_m", ctypes.c_int64), ("band_grid", ctypes.c_int64),
-        ("tail_ring", ctypes.c_int32),
+        ("tail_ring", ctypes.c_int32), ("half_stage_slots", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:

@@ -266,6 +266,13 @@ static int make_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, i
     p.b_stage_bytes = p.BK * p.BN * elt;
     p.stage_bytes = p.a_stage_bytes + p.b_stage_bytes;
     p.lds_bytes = stages * p.stage_bytes;
+    // A DIRECT ring of S stages that does not fit, of a tile whose A and B parts are the
+    // same size, runs as 2S - 1 half-stage slots (the kernel's half-stage ring).
+    if (variant == V_DIRECT && p.lds_bytes > kLdsPerCu && p.a_stage_bytes == p.b_stage_bytes &&
+        (2 * stages - 1) * p.a_stage_bytes <= kLdsPerCu) {
+        p.half_stage_slots = 2 * stages - 1;
+        p.lds_bytes = p.half_stage_slots * p.a_stage_bytes;
+    }
     if (p.lds_bytes > kLdsPerCu)
         return fail(SPT_ERR_UNSUPPORTED, "a %d-stage ring of %d-byte stages exceeds the 160 KiB of LDS", stages,
                     p.stage_bytes);
@@ -276,6 +283,8 @@ static int make_plan(int dtype, int64_t M, int64_t N, int64_t K, int b_layout, i
     p.wg_per_cu_lds = kLdsPerCu / p.lds_bytes;
     p.waves_per_simd_lds = p.wg_per_cu_lds * p.waves / kSimdsPerCu;
     p.steady_vmcnt = variant == V_DIRECT ? (stages - 2) * (p.a_copies_per_thread + p.b_copies_per_thread) : 0;
+    if (p.half_stage_slots)  // B of the next tile landed, A of the tile after it in flight
+        p.steady_vmcnt = (p.half_stage_slots - 4) * p.a_copies_per_thread;
     if (variant == V_PERSIST)  // the younger copies, and the stores issued after the awaited copies
         p.steady_vmcnt = (stages - 2) * (p.a_copies_per_thread + p.b_copies_per_thread) +
                          (stages - 1) * ((p.wave_m / 16) * (p.wave_n / 16) / p.store_window);

@@ -71,6 +71,9 @@ constexpr KernelEntry pentry()
 
 #define SPT_TILE_ALL(DT, BC, TI) SPT_PAIRS(DT, BC, TI), SPT_RING34(DT, BC, TI), SPT_EXACT(DT, BC, TI), SPT_EXACT34(DT, BC, TI)
 #define SPT_TILE_BIG(DT, BC, TI) SPT_PAIRS(DT, BC, TI), SPT_EXACT(DT, BC, TI)
+// The 3-stage rings of the 256 x 256 x 128-byte tiles, as 5 half-stage slots.
+#define SPT_HALF(DT, BC) entry<DT, BC, 4, V_DIRECT, 3>(), entry<DT, BC, 4, V_DIRECT, 3, 1>(), \
+        entry<DT, BC, 2, V_DIRECT, 3>(), entry<DT, BC, 2, V_DIRECT, 3, 1>()
 
 // The table of one (element type, B layout): NAME is e.g. f16_row.  Race-detection
 // builds (SPT_POISON) hold the ring kernels only: DIRECT on every tile and PERSIST.
@@ -80,11 +83,12 @@ constexpr KernelEntry pentry()
     SPT_RING_ONLY(DT, BC, 1), SPT_RING34(DT, BC, 1), SPT_EXACT34(DT, BC, 1), SPT_RING_ONLY(DT, BC, 2),   \
         entry<DT, BC, 3, V_DIRECT, 2>(), SPT_RING34(DT, BC, 3), SPT_RING_ONLY(DT, BC, 4),               \
         SPT_RING_ONLY(DT, BC, 5), SPT_RING34(DT, BC, 5), SPT_EXACT34(DT, BC, 5), SPT_RING_ONLY(DT, BC, 6),  \
-        SPT_PERSIST(DT, BC)
+        SPT_HALF(DT, BC), SPT_PERSIST(DT, BC)
 #else
 #define SPT_TABLE_ENTRIES(DT, BC)                                                                      \
     SPT_TILE_ALL(DT, BC, 1), SPT_TILE_BIG(DT, BC, 2), SPT_PAIRS(DT, BC, 3), SPT_RING34(DT, BC, 3),      \
-        SPT_TILE_BIG(DT, BC, 4), SPT_TILE_ALL(DT, BC, 5), SPT_TILE_BIG(DT, BC, 6), SPT_PERSIST(DT, BC)
+        SPT_TILE_BIG(DT, BC, 4), SPT_TILE_ALL(DT, BC, 5), SPT_TILE_BIG(DT, BC, 6), SPT_HALF(DT, BC),      \
+        SPT_PERSIST(DT, BC)
 #endif
 #define SPT_DEFINE_TABLE(NAME, DT, BC)                                                          \
     static const KernelEntry k_##NAME[] = {                                                    \

@@ -133,10 +133,23 @@ struct Cfg {
     static constexpr int A_BYTES = BM * BK * ELT;
     static constexpr int B_BYTES = BK * BN * ELT;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int LDS_BYTES = S * STAGE_BYTES;
+    // Half-stage ring: S full stages of a tile whose A and B parts are the same size
+    // that do not fit in LDS (3 x 64 KiB for the 256 x 256 x 128-byte tiles) run as
+    // 2S - 1 half-stage slots instead, each holding the A or the B part of one K tile.
+    // Ring position 2t holds A of tile t, 2t + 1 its B, in slot (position mod 2S - 1).
+    static constexpr bool SPLIT = V_ == V_DIRECT && A_BYTES == B_BYTES && S_ * STAGE_BYTES > kLdsPerCu &&
+                                  (2 * S_ - 1) * A_BYTES <= kLdsPerCu;
+    static constexpr int SLOTS = SPLIT ? 2 * S_ - 1 : 2 * S_;  // half-stage slots of the ring
+    static constexpr int LDS_BYTES = SPLIT ? SLOTS * A_BYTES : S * STAGE_BYTES;
     static constexpr int A_CPT = A_BYTES / 16 / THREADS;  // 16-byte copies per thread per stage
     static constexpr int B_CPT = B_BYTES / 16 / THREADS;
     static constexpr int LOADS = A_CPT + B_CPT;            // vmcnt units per tile per thread
+    // Copies of younger tiles that may stay in flight per thread: at the wait that
+    // closes a K tile (the next tile must have landed) and after the prologue (tile
+    // 0 must have landed).  A half-stage ring issues B of a tile before A of the
+    // next one, so one half stage (A of the tile after next) stays in flight.
+    static constexpr int VM_STEADY = SPLIT ? (SLOTS - 4) * A_CPT : (S_ - 2) * LOADS;
+    static constexpr int VM_FIRST = SPLIT ? (SLOTS - 2) * A_CPT : (S_ - 1) * LOADS;
     // 16x16 wave tiles of 128 x 128 need the whole register file: one wave per
     // SIMD; so does a ring that leaves LDS for one workgroup of four waves per CU
     static constexpr int WG_PER_CU_LDS = kLdsPerCu / LDS_BYTES;
@@ -152,6 +165,7 @@ struct Cfg {
     static_assert(V_ != V_SYNC || S_ == 1, "SYNC has one stage");
     static_assert(V_ != V_REG || (S_ == 1 || S_ == 2), "REG has 1 or 2 stages");
     static_assert(V_ != V_DIRECT || (S_ >= 2 && S_ <= 4), "DIRECT has 2 to 4 stages");
+    static_assert(!SPLIT || (!RING_TAIL && A_CPT == B_CPT), "half-stage rings: equal halves, no in-ring tail");
     static_assert(V_ != V_PERSIST || (S_ >= 2 && S_ <= 4 && EXACT_), "PERSIST: exact-fit 2- to 4-stage rings");
     static_assert((S_ - 1) * LOADS < 64, "vmcnt range");
 };
@@ -337,6 +351,9 @@ struct Gemm {
     static constexpr int BQ_ = C::ELT == 2 && !WIDE16 ? 4 : 8;
     static constexpr int BQ = C::FN % BQ_ == 0 ? BQ_ : C::FN;
     static constexpr int B_OFFS = C::BCOL ? C::KS : (C::BLANE ? 1 : BQ);
+    // B's lane offsets count from the start of B's region: A_BYTES into a full stage,
+    // 0 into a half-stage slot
+    static constexpr int B_OFF = C::SPLIT ? 0 : C::A_BYTES;
     struct Lanes {
         int a[C::KS];
         int b[B_OFFS];
@@ -348,10 +365,10 @@ struct Gemm {
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) {
             L.a[s] = (16 * mb0 + l16) * RK + 16 * ((4 * s + g) ^ swz_k(l16));
-            if constexpr (C::BCOL) L.b[s] = C::A_BYTES + (16 * nb0 + l16) * RK + 16 * ((4 * s + g) ^ swz_k(l16));
+            if constexpr (C::BCOL) L.b[s] = B_OFF + (16 * nb0 + l16) * RK + 16 * ((4 * s + g) ^ swz_k(l16));
         }
         if constexpr (!C::BCOL && C::BLANE) {
-            L.b[0] = br_block(nb0, 0, 0) + lane * (C::ELT == 4 ? 4 : 8);
+            L.b[0] = br_block(nb0, 0, 0) - C::A_BYTES + B_OFF + lane * (C::ELT == 4 ? 4 : 8);
         } else if constexpr (!C::BCOL && C::ELT == 2) {
             // tr_b16: lane (g, i) fetches k-row 8g + (i >> 2) (+ 4h + KSTEP s) at columns
             // 4 (i & 3) .. + 3 of column block nb; swz_n only sees k-row bits 0, 1 and 3,
@@ -360,7 +377,7 @@ struct Gemm {
             for (int n = 0; n < BQ; ++n) {
                 const int kr = 8 * g + (l16 >> 2);
                 const int c = 2 * (nb0 + n) + ((l16 & 3) >> 1);
-                L.b[n] = C::A_BYTES + kr * RN + 16 * (c ^ swz_n(kr)) + 8 * (l16 & 1);
+                L.b[n] = B_OFF + kr * RN + 16 * (c ^ swz_n(kr)) + 8 * (l16 & 1);
             }
         } else if constexpr (!C::BCOL && C::ELT == 1) {
             // tr_b8: lane (g, i) fetches k-row 16g + (i >> 1) (+ 8h + KSTEP s) at columns
@@ -368,7 +385,7 @@ struct Gemm {
 #pragma unroll
             for (int n = 0; n < BQ; ++n) {
                 const int kr = 16 * g + (l16 >> 1);
-                L.b[n] = C::A_BYTES + kr * RN + 16 * ((nb0 + n) ^ swz_n(kr)) + 8 * (l16 & 1);
+                L.b[n] = B_OFF + kr * RN + 16 * ((nb0 + n) ^ swz_n(kr)) + 8 * (l16 & 1);
             }
         }
     }
@@ -513,8 +530,11 @@ struct Gemm {
         i32x4_t qa, qb;    // descriptors of the next K tile to copy: base - DMA_BIAS, extent
         uint64_t sa, sb;   // bytes between consecutive K tiles
         uint32_t na, nb;   // extent (with DMA_BIAS) of a full K tile
-        int left;          // K tiles not yet copied (the in-ring partial tile included)
+        int left;          // K tiles not yet copied (the in-ring partial tile included); of B
+                           // in a half-stage ring, whose A runs one tile ahead
+        int left_a;        // half-stage ring: K tiles of A not yet copied
         uint32_t m0a, m0b; // LDS byte address of this wave's first A / B block in stage 0
+                           // (half-stage ring: in slot 0)
         uint32_t tail_b;   // extent of the partial tile's row-major B copies (else nb)
     };
     static __device__ __forceinline__ i32x4_t desc(uint64_t base, uint32_t bytes)
@@ -551,11 +571,12 @@ struct Gemm {
             // the partial tile's copies of row-major B end after its k_tail rows: the
             // rows past K read as zeros
             if (tail) r.tail_b = (uint32_t)(((long long)p.k_tail * p.ldb - n0) * C::ELT) + DMA_BIAS;
+        r.left_a = r.left;
         r.qa = desc(a, r.left > 0 ? r.na : 0u);
         r.qb = desc(b, r.left > 0 ? (r.left == 1 ? r.tail_b : r.nb) : 0u);
         const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
         r.m0a = lds0 + (uint32_t)(wave * C::A_CPT) * 1024u;
-        r.m0b = lds0 + (uint32_t)C::A_BYTES + (uint32_t)(wave * C::B_CPT) * 1024u;
+        r.m0b = lds0 + (uint32_t)(C::SPLIT ? 0 : C::A_BYTES) + (uint32_t)(wave * C::B_CPT) * 1024u;
     }
     // Ring bookkeeping after a tile's copies were taken, in three parts that
     // the scheduler spreads over free MFMA slots: advance the A base, the B
@@ -573,9 +594,23 @@ struct Gemm {
         if (part == 1) add64(r.qb, r.sb);
         if (part == 2) {
             r.left -= 1;
-            r.qa[2] = (int)(r.left > 0 ? r.na : 0u);
+            if constexpr (C::SPLIT) r.left_a -= 1;
+            r.qa[2] = (int)((C::SPLIT ? r.left_a : r.left) > 0 ? r.na : 0u);
             r.qb[2] = (int)(r.left > 1 ? r.nb : r.left == 1 ? r.tail_b : 0u);
         }
+    }
+    // Half-stage ring prologue: one operand's copy taken, advance that operand alone.
+    static __device__ __forceinline__ void ring_advance_a(Ring& r)
+    {
+        add64(r.qa, r.sa);
+        r.left_a -= 1;
+        r.qa[2] = (int)(r.left_a > 0 ? r.na : 0u);
+    }
+    static __device__ __forceinline__ void ring_advance_b(Ring& r)
+    {
+        add64(r.qb, r.sb);
+        r.left -= 1;
+        r.qb[2] = (int)(r.left > 0 ? r.nb : 0u);
     }
 
 #ifdef SPT_POISON
@@ -586,16 +621,20 @@ struct Gemm {
     // copies land then shows up in C as NaN, or as a wrong int8 sum.
     static __device__ __forceinline__ void poison(const Ring& r, uint32_t stage_off)
     {
+        poison(r, stage_off, stage_off);
+    }
+    static __device__ __forceinline__ void poison(const Ring& r, uint32_t a_off, uint32_t b_off)
+    {
         constexpr int pv = C::DT == DT_F16 ? 0x7E007E00 : C::DT == DT_BF16 ? 0x7FC07FC0
                            : C::DT == DT_F32 ? 0x7FC00000 : 0x7F7F7F7F;
         const i32x4_t v = {pv, pv, pv, pv};
         const uint32_t lane = (threadIdx.x & 63) * 16;
 #pragma unroll
         for (int i = 0; i < C::A_CPT; ++i)
-            *(SPT_LDS i32x4_t*)(size_t)(r.m0a + stage_off + i * 1024 + lane) = v;
+            *(SPT_LDS i32x4_t*)(size_t)(r.m0a + a_off + i * 1024 + lane) = v;
 #pragma unroll
         for (int i = 0; i < C::B_CPT; ++i)
-            *(SPT_LDS i32x4_t*)(size_t)(r.m0b + stage_off + i * 1024 + lane) = v;
+            *(SPT_LDS i32x4_t*)(size_t)(r.m0b + b_off + i * 1024 + lane) = v;
         wait_lgkmcnt0();
     }
 #endif
@@ -610,11 +649,16 @@ struct Gemm {
     {
         return Dma{r.qa, r.qb, r.m0a + stage_off, r.m0b + stage_off};
     }
+    static __device__ __forceinline__ Dma dma_of(const Ring& r, uint32_t a_off, uint32_t b_off)
+    {
+        return Dma{r.qa, r.qb, r.m0a + a_off, r.m0b + b_off};
+    }
+    // (a half-stage ring issues the B copies first: see VM_STEADY)
     template <int J>
     static __device__ __forceinline__ void dma_issue(const Dma& d, const Copy& cp)
     {
-        constexpr bool IS_A = J < C::A_CPT;
-        constexpr int i = IS_A ? J : J - C::A_CPT;  // copy index within the operand
+        constexpr bool IS_A = C::SPLIT ? J >= C::B_CPT : J < C::A_CPT;
+        constexpr int i = C::SPLIT ? (IS_A ? J - C::B_CPT : J) : (IS_A ? J : J - C::A_CPT);  // copy index within the operand
         constexpr int g = i / 4, e = i % 4;          // group of four sharing one M0 value
         const uint32_t m0 = (IS_A ? d.m0a : d.m0b) + g * 4096;
         if constexpr (IS_A)
@@ -698,18 +742,36 @@ struct Gemm {
 
     // ---- consumer ----------------------------------------------------------------
     // Fragment read j (0 .. FM+FN-1) of k-step s into `slot`.
+    // B of a full stage at st: st + A_BYTES
+    static __device__ __forceinline__ const SPT_LDS char* b_of(const SPT_LDS char* st)
+    {
+        return st + (C::A_BYTES - B_OFF);
+    }
     static __device__ __forceinline__ void read_frag(const SPT_LDS char* st, const Lanes& L, int s, int j,
                                                      Slot& slot)
     {
+        read_frag(st, b_of(st), L, s, j, slot);
+    }
+    // A from the stage or slot at sa; B at the base its lane offsets count from, sb
+    // (b_of(st) for a full stage at st, the slot itself in a half-stage ring)
+    static __device__ __forceinline__ void read_frag(const SPT_LDS char* sa, const SPT_LDS char* sb, const Lanes& L,
+                                                     int s, int j, Slot& slot)
+    {
         if (j < C::FM)
-            slot[j] = read_a(st, L, j, s);
+            slot[j] = read_a(sa, L, j, s);
         else
-            slot[j] = read_b(st, L, j - C::FM, s);
+            slot[j] = read_b(sb, L, j - C::FM, s);
     }
     static __device__ __forceinline__ void read_slot(const SPT_LDS char* st, const Lanes& L, int s, Slot& slot)
     {
 #pragma unroll
-        for (int j = 0; j < C::FM + C::FN; ++j) read_frag(st, L, s, j, slot);
+        for (int j = 0; j < C::FM + C::FN; ++j) read_frag(st, b_of(st), L, s, j, slot);
+    }
+    static __device__ __forceinline__ void read_slot(const SPT_LDS char* sa, const SPT_LDS char* sb, const Lanes& L,
+                                                     int s, Slot& slot)
+    {
+#pragma unroll
+        for (int j = 0; j < C::FM + C::FN; ++j) read_frag(sa, sb, L, s, j, slot);
     }
     static __device__ __forceinline__ void mma_one(const Slot& slot, int j, acc_t (&acc)[C::FM][C::FN])
     {
@@ -784,14 +846,21 @@ struct Gemm {
                                                 int snext, const Dma& d, const Copy& cp, Ring& r,
                                                 acc_t (&acc)[C::FM][C::FN])
     {
+        step<NDMA, READ, ADV>(use, nxt, src, b_of(src), L, snext, d, cp, r, acc);
+    }
+    template <int NDMA, bool READ, bool ADV>
+    static __device__ __forceinline__ void step(const Slot& use, Slot& nxt, const SPT_LDS char* src,
+                                                const SPT_LDS char* srcb, const Lanes& L, int snext, const Dma& d,
+                                                const Copy& cp, Ring& r, acc_t (&acc)[C::FM][C::FN])
+    {
         static_assert(!ADV || NDMA > 0, "bookkeeping belongs to the step that copies");
         static_for<0, NJ>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
             constexpr int dj = dma_owner(j, NDMA), aj = a_owner(j), qj = adv_owner(j, NDMA);
             mma_one(use, j, acc);
             if constexpr (dj >= 0) dma_issue<dj>(d, cp);
-            if constexpr (READ && j < C::FN) read_frag(src, L, snext, C::FM + j, nxt);
-            if constexpr (READ && aj >= 0) read_frag(src, L, snext, aj, nxt);
+            if constexpr (READ && j < C::FN) read_frag(src, srcb, L, snext, C::FM + j, nxt);
+            if constexpr (READ && aj >= 0) read_frag(src, srcb, L, snext, aj, nxt);
             if constexpr (ADV && qj >= 0) ring_advance(r, qj);
             order_fence();
         });
@@ -904,7 +973,7 @@ struct Gemm {
             ring_advance(r, 1);
             ring_advance(r, 2);
         }
-        wait_vmcnt<(C::S - 1) * C::LOADS>();  // tile 0 landed
+        wait_vmcnt<C::VM_FIRST>();  // tile 0 landed
         barrier();
         Slot sl[2];
         read_slot(smem, L, 0, sl[0]);
@@ -942,7 +1011,7 @@ struct Gemm {
                 step<0, true, false>(use, nxt, smem + rs, L, s + 1, none, cp, r, acc);
             } else {
                 wait_lgkmcnt0();                       // this wave's reads of this tile are complete
-                wait_vmcnt<(C::S - 2) * C::LOADS>();   // its copies of the next tile have landed
+                wait_vmcnt<C::VM_STEADY>();            // its copies of the next tile have landed
                 barrier();                             // next tile visible to all; this stage free
                 if constexpr (C::RING_TAIL)
                     if (r.left == 1 && p.tail_ring) mask_tail(p, threadIdx.x, cp);  // tile + S is the partial one
@@ -954,6 +1023,72 @@ struct Gemm {
             }
         });
         rs = nx;
+    }
+
+    // Half-stage ring (C::SPLIT): SLOTS = 2S - 1 slots of A_BYTES; ring position 2t
+    // holds A of K tile t, 2t + 1 its B, in slot (position mod SLOTS).  The prologue
+    // copies positions 0 .. SLOTS-1.  At the barrier of tile t (the schedule of
+    // loop_direct) tile t's two slots are free, and the next two positions go into
+    // them: B of tile t + S - 1 into A's slot, then A of tile t + S into B's.  The
+    // wait before that barrier needs tile t + 1 (positions up to 2t + 3); the copies
+    // issued after it, A of tile t + 2, may stay in flight: the copy path never
+    // drains, which a 2-stage ring of the same tile does at every K tile.
+    static __device__ __forceinline__ void loop_split(const GemmArgs& p, int m0, int n0, int wave,
+                                                      const Lanes& L, SPT_LDS char* smem, Copy& cp,
+                                                      acc_t (&acc)[C::FM][C::FN])
+    {
+        static_assert(C::KS % 2 == 0, "half-stage rings: an even number of k-steps per K tile");
+        constexpr uint32_t HB = C::A_BYTES;
+        const int nf = p.k_full;
+        if (nf == 0) return;
+        Ring r;
+        ring_init(p, m0, n0, wave, smem, r);
+        static_for<0, C::SLOTS>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            const Dma d = dma_of(r, i * HB, i * HB);
+            if constexpr (i % 2 == 0) {
+                static_for<C::B_CPT, C::LOADS>([&](auto jc) { dma_issue<decltype(jc)::value>(d, cp); });
+                ring_advance_a(r);
+            } else {
+                static_for<0, C::B_CPT>([&](auto jc) { dma_issue<decltype(jc)::value>(d, cp); });
+                ring_advance_b(r);
+            }
+        });
+        wait_vmcnt<C::VM_FIRST>();  // tile 0 landed
+        barrier();
+        Slot sl[2];
+        read_slot(smem, smem + HB, L, 0, sl[0]);
+        uint32_t ao = 0, bo = HB;  // slots of tile t's A and B
+        for (int t = 0; t < nf; ++t) tile_split(r, ao, bo, L, smem, cp, sl, acc);
+        wait_vmcnt<0>();  // no copy may still be writing this workgroup's LDS
+    }
+    static __device__ __forceinline__ void tile_split(Ring& r, uint32_t& ao, uint32_t& bo, const Lanes& L,
+                                                      const SPT_LDS char* smem, Copy& cp, Slot (&sl)[2],
+                                                      acc_t (&acc)[C::FM][C::FN])
+    {
+        constexpr uint32_t HB = C::A_BYTES, WRAP = C::SLOTS * HB;
+        const uint32_t an = ao + 2 * HB >= WRAP ? ao + 2 * HB - WRAP : ao + 2 * HB;
+        const uint32_t bn = bo + 2 * HB >= WRAP ? bo + 2 * HB - WRAP : bo + 2 * HB;
+        const Dma none{};
+        static_for<0, C::KS>([&](auto sc) {
+            constexpr int s = decltype(sc)::value;
+            Slot& use = sl[s & 1];
+            Slot& nxt = sl[(s + 1) & 1];
+            if constexpr (s + 1 < C::KS) {
+                step<0, true, false>(use, nxt, smem + ao, smem + bo, L, s + 1, none, cp, r, acc);
+            } else {
+                wait_lgkmcnt0();                 // this wave's reads of this tile are complete
+                wait_vmcnt<C::VM_STEADY>();      // its copies of the next tile have landed
+                barrier();                       // next tile visible to all; this tile's slots free
+                const Dma d = dma_of(r, bo, ao); // A of tile + S into B's slot, B of tile + S - 1 into A's
+#ifdef SPT_POISON
+                poison(r, bo, ao);
+#endif
+                step<C::LOADS, true, true>(use, nxt, smem + an, smem + bn, L, 0, d, cp, r, acc);
+            }
+        });
+        ao = an;
+        bo = bn;
     }
 
     static __device__ __forceinline__ void run(const GemmArgs& p)
@@ -1017,6 +1152,8 @@ struct Gemm {
                 wait_lgkmcnt0();
                 barrier();
             }
+        } else if constexpr (C::SPLIT) {
+            loop_split(p, m0, n0, wave, L, smem, cp, acc);
         } else {
             loop_direct(p, m0, n0, wave, L, smem, cp, acc);
         }

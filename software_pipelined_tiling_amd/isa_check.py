@@ -23,14 +23,16 @@ counts.  `check(kernel)` turns that into pass/fail properties:
     counts     MFMAs, copies and barriers per iteration match the plan
     vmcnt      one vmcnt wait per tile, each (S-2) x copies-per-tile: the
                copies of younger tiles stay in flight (for S >= 3 there is
-               no vmcnt(0) in the steady state)
+               no vmcnt(0) in the steady state); a 3-stage ring run as 5
+               half-stage slots keeps half a tile's copies in flight
+               (copies-per-tile / 2)
     lgkmcnt    one lgkmcnt(0) per tile (before the barrier); every other
                lgkm wait is partial, so fragment reads overlap the MFMAs
     overlap    every copy sits in an MFMA gap of its own (none in the
                barrier's gap) and no gap holds more than 3 fragment reads:
                loads are interleaved with the MFMAs, not bunched
     clean      no scratch access and no accumulator copies in the loop
-    lds        LDS size = S x stage bytes
+    lds        LDS size = S x stage bytes (2S - 1 half stages for such a ring)
   SYNC: the loop drains vmcnt(0) before its first MFMA (no overlap: the
   unpipelined reference).  REG: the tile's global loads are issued before the
   first MFMA of the iteration and their vmcnt wait comes after the last one.
@@ -67,6 +69,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 TILES = {1: (128, 256, 64, 2, 2), 2: (256, 256, 128, 2, 4), 3: (128, 128, 64, 2, 2),
          4: (256, 256, 128, 2, 2), 5: (256, 256, 64, 2, 2), 6: (256, 192, 128, 2, 4)}
 ELT = {0: 2, 1: 2, 2: 1, 3: 4}
+LDS_PER_CU = 163840
 VARIANTS = {1: "sync", 2: "reg", 3: "direct"}
 _CFG = re.compile(r"CfgILi(\d+)ELb(\d)ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)ELb(\d)E")
 
@@ -93,7 +96,14 @@ class Kernel:
         mfma = fm * fn * ks * (4 if self.dtype == 3 else 1)
         loads = (BM * BKB + BKB * BN) // 16 // (64 * waves)
         stage = BM * BKB + BKB * BN
-        return dict(mfma_per_tile=mfma, loads_per_tile=loads, ks=ks, stage_bytes=stage,
+        # a DIRECT ring of S full stages that exceed the LDS, with A and B parts of one size,
+        # runs as 2S - 1 half-stage slots; the copies of one half stay in flight per wait
+        half = (self.variant == "direct" and self.stages * stage > LDS_PER_CU and BM == BN
+                and (2 * self.stages - 1) * stage // 2 <= LDS_PER_CU)
+        lds = (2 * self.stages - 1) * stage // 2 if half else self.stages * stage
+        steady = (2 * self.stages - 5) * loads // 2 if half else (self.stages - 2) * loads
+        return dict(mfma_per_tile=mfma, loads_per_tile=loads, ks=ks, stage_bytes=stage, lds_bytes=lds,
+                    steady_vmcnt=steady, half_stage_slots=2 * self.stages - 1 if half else 0,
                     tiles_per_iter=1 if ks % 2 == 0 or self.variant != "direct" else 2)
 
 
@@ -469,15 +479,14 @@ def check(k: Kernel) -> Dict[str, bool]:
     if k.variant == "direct":
         res["counts"] = (st["mfma"] == T * g["mfma_per_tile"] and st["dma"] == T * g["loads_per_tile"]
                          and st["barriers"] == T)
-        res["vmcnt"] = len(st["vmcnt_waits"]) == T and all(
-            v == (k.stages - 2) * g["loads_per_tile"] for v in st["vmcnt_waits"])
+        res["vmcnt"] = len(st["vmcnt_waits"]) == T and all(v == g["steady_vmcnt"] for v in st["vmcnt_waits"])
         res["lgkmcnt"] = st["lgkmcnt_waits"].count(0) == T
         # each copy in an MFMA gap of its own, none in the gap of the barrier, fragment
         # reads at most 3 to a gap (a 16-cycle MFMA leaves about three issue slots)
         res["overlap"] = (st["dma_per_gap_max"] == 1 and st["dma_in_barrier_gap"] == 0
                           and st["ds_reads_per_gap_max"] <= 3)
         res["clean"] = st["scratch"] == 0 and st["acc_moves"] == 0
-        res["lds"] = k.meta.get("lds") == k.stages * g["stage_bytes"]
+        res["lds"] = k.meta.get("lds") == g["lds_bytes"]
     elif k.variant == "sync":
         res["no_overlap"] = st["vmcnt0_before_first_mfma"]
         res["lds"] = k.meta.get("lds") == g["stage_bytes"]

@@ -62,8 +62,7 @@ def ex(M=64, N=64, K=64, A=PA, lda=None, B=PB, ldb=None, C=PC, ldc=None, dtype=s
     (dict(lda=32), -1), (dict(ldb=32), -1), (dict(ldc=8), -1), (dict(lay=spt.COL, ldb=32), -1),
     (dict(var=spt.VARIANT_SYNC, st=2), -2), (dict(var=spt.VARIANT_DIRECT, st=1), -2),
     (dict(var=spt.VARIANT_REG, st=3), -2), (dict(dtype=spt.I8, K=131072), -2),
-    (dict(var=spt.VARIANT_DIRECT, st=3, tile=spt.TILE_256x256), -2),
-    (dict(var=spt.VARIANT_DIRECT, st=3, tile=spt.TILE_256x256_4W), -2), (dict(tile=7), -1),
+    (dict(var=spt.VARIANT_DIRECT, st=4, tile=spt.TILE_256x256_4W), -2), (dict(tile=7), -1),
     (dict(var=spt.VARIANT_DIRECT, st=3, tile=spt.TILE_256x192), -2),
     (dict(var=spt.VARIANT_DIRECT, st=4, tile=spt.TILE_256x256), -2),
     (dict(A=0x8000), -2), (dict(B=1 << 47), -2),
@@ -117,9 +116,17 @@ def test_plan_matches_page_formulas(L, dtype, elt, tile, var, st):
     BK = BKB // elt
     M, N, K = 4000, 3000, 1000
     rc, pi = spt.spt_plan(dtype, M, N, K, spt.ROW, var, st, tile)
+    half = BM * BKB  # bytes of one operand's part of a stage
     if P.ring_bytes(BM, BN, BKB // elt, elt, st) > 163840:  # the ring does not fit in LDS
+        if var == spt.VARIANT_DIRECT and BM == BN and (2 * st - 1) * half <= 163840:
+            # ... but its 2S - 1 half stages do (A and B parts of one size)
+            assert rc == 0 and pi.half_stage_slots == 2 * st - 1 and pi.lds_bytes == (2 * st - 1) * half
+            assert pi.steady_vmcnt == (2 * st - 5) * pi.a_copies_per_thread
+            assert pi.a_copies_per_thread == pi.b_copies_per_thread == P.copies_per_thread(BM, BKB // elt, elt, thr)
+            return
         assert rc == -2
         return
+    assert pi.half_stage_slots == 0
     assert rc == 0
     assert (pi.BM, pi.BN, pi.BK, pi.threads) == (BM, BN, BK, thr)
     assert pi.stage_bytes == P.stage_bytes(BM, BN, BK, elt)

@@ -27,9 +27,14 @@ SENT_I = np.int32(0x7FFFFFFF)
 
 
 def built(tile, variant, stages):
-    """Rings of 64 KiB and 56 KiB stages (tiles 2, 4 and 6) hold two stages at most in
-    160 KiB of LDS."""
-    return not (tile in (2, 4, 6) and variant == "direct" and stages >= 3)
+    """Rings of 64 KiB and 56 KiB stages (tiles 2, 4 and 6) hold two full stages at most
+    in 160 KiB of LDS; the 256 x 256 x 128-byte tiles (2, 4) run 3 stages as 5
+    half-stage slots."""
+    if variant != "direct" or stages < 3:
+        return True
+    if tile in (2, 4):
+        return stages == 3
+    return tile != 6
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -191,6 +196,32 @@ def test_partial_tile_through_the_ring(oracle_mod, dtype, b_col, tile):
             assert np.array_equal(C.view(np.uint32), C1.view(np.uint32)), (tile, st, K)
 
 
+HALF_RING_SHAPES = [(256, 256, 1), (512, 256, 2), (256, 512, 3), (512, 512, 4), (256, 768, 5), (768, 256, 8)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8", "f32"])
+@pytest.mark.parametrize("b_col", [False, True])
+@pytest.mark.parametrize("tile", [2, 4])
+def test_half_stage_ring(oracle_mod, dtype, b_col, tile):
+    """The 3-stage ring of the 256 x 256 x 128-byte tiles runs as 5 half-stage slots (A
+    and B of a K tile in separate slots, the copies of the next A kept in flight at
+    every wait).  Exact-fit shapes with 1 to 8 K tiles (the prologue copies past the
+    last tile are empty) and a ragged one with a K tail (general kernels): the results
+    agree with the oracle and bit for bit with the 2-stage ring."""
+    BK = 128 // I.ELT_BYTES[dtype]
+    cases = [(M, N, kt * BK) for M, N, kt in HALF_RING_SHAPES] + [(300, 600, 3 * BK + 5)]
+    for i, (M, N, K) in enumerate(cases):
+        rc, pi = spt.spt_plan(spt.DTYPE_CODES[dtype], M, N, K, spt.COL if b_col else spt.ROW,
+                              spt.VARIANT_DIRECT, 3, tile)
+        assert rc == 0 and pi.half_stage_slots == 5 and pi.lds_bytes == 5 * pi.a_stage_bytes
+        A, B = operands(dtype, b_col, M, N, K, 40 + i, lda_pad=8, ldb_pad=8)
+        Cref = ref(oracle_mod, A, B, dtype, b_col, N, K)
+        C3 = run(A, B, dtype, b_col, M, N, K, "direct", 3, tile)
+        parity.check_full(C3, Cref, A, B, dtype, b_col, M, N, K)
+        C2 = run(A, B, dtype, b_col, M, N, K, "direct", 2, tile)
+        assert np.array_equal(C3.view(np.uint32), C2.view(np.uint32)), (tile, M, N, K)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
 def test_integer_valued_bit_exact(oracle_mod, dtype):
     """Integer inputs (|a|,|b| <= 4; int8 full range): every partial sum is exact in the
@@ -333,7 +364,7 @@ def test_full_fp16_4096(oracle_mod, variant, stages):
     sampled(oracle_mod, I.W_F16_4096, variant, stages, 1)
 
 
-@pytest.mark.parametrize("tile,stages", [(2, 2), (4, 2), (5, 2), (5, 3), (5, 4), (1, 4), (6, 2)])
+@pytest.mark.parametrize("tile,stages", [(2, 2), (2, 3), (4, 2), (4, 3), (5, 2), (5, 3), (5, 4), (1, 4), (6, 2)])
 def test_full_fp16_4096_ring_tiles(oracle_mod, tile, stages):
     """The ring kernels of the other tiles at the full 4096^3 size (exact-fit,
     except the 256 x 192 tile, whose grid has a ragged last column)."""

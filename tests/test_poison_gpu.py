@@ -52,7 +52,8 @@ def poisoned(L, A, B, dtype, b_col, M, N, K, variant, stages, tile):
     return C.cpu().numpy()
 
 
-RINGS = [(1, 2), (1, 3), (1, 4), (2, 2), (3, 2), (3, 3), (3, 4), (4, 2), (5, 2), (5, 3), (5, 4), (6, 2)]
+RINGS = [(1, 2), (1, 3), (1, 4), (2, 2), (2, 3), (3, 2), (3, 3), (3, 4), (4, 2), (4, 3), (5, 2), (5, 3), (5, 4),
+         (6, 2)]
 
 
 @pytest.mark.parametrize("dtype,b_col", [("f16", False), ("i8", True)])
