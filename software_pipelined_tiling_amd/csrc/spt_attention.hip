@@ -277,7 +277,7 @@ struct Attn {
 
     // One key block from the stage at `st`: S = Q K^T, online softmax, O += P V.
     // `mid` runs between S = Q K^T and the softmax, once the K fragments are dead.
-    template <class F>
+    template <bool MASK, class F>
     static __device__ __forceinline__ void block(const AttnArgs& p, const SPT_LDS char* st, const Lanes& L,
                                                  const i32x4_t (&qf)[C::FM][C::KS], acc_t (&o)[C::FM][C::DN],
                                                  float (&mrun)[C::FM], float (&lrun)[C::FM], int t, int lane, F&& mid)
@@ -302,22 +302,17 @@ struct Attn {
 
         mid();
 
-        // logits x = c * S in the base-2 domain; keys past Sk get -inf
-#pragma unroll
-        for (int m = 0; m < C::FM; ++m)
-#pragma unroll
-            for (int n = 0; n < C::NB; ++n) s[m][n] *= p.c;  // logits, then probabilities, in place
-        if (t * C::BKV + C::BKV > p.Sk) {  // the ragged last block (wave-uniform)
-            const int lim = p.Sk - t * C::BKV - 4 * (lane >> 4);  // keys 16 n + e < lim are inside Sk
-#pragma unroll
-            for (int m = 0; m < C::FM; ++m)
-#pragma unroll
-                for (int n = 0; n < C::NB; ++n)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (16 * n + e >= lim) s[m][n][e] = -INFINITY;
-        }
-        float bmax[C::FM];
+        // The scores stay unscaled until the exponent: the test below compares c max S
+        // (c >= 0; rounding is monotonic, so that is the largest rounded logit c S) with
+        // the reference, and each probability is 2^(x - m) with x = c S rounded first, so
+        // that the logit equal to the reference gives exactly 1.  MASK (the last block):
+        // keys past Sk get no maximum and weight 0.
+        const int lim = p.Sk - t * C::BKV - 4 * (lane >> 4);  // keys 16 n + e < lim are inside Sk
+        // Each lane tests its own logits against the reference: a row needs a new one
+        // when any of its logits exceeds the reference by more than kSlack, which the
+        // wave learns from one ballot; only then are the row maxima reduced across the
+        // row's four lanes.
+        float lmax[C::FM];
         bool up = false;
 #pragma unroll
         for (int m = 0; m < C::FM; ++m) {
@@ -325,9 +320,9 @@ struct Attn {
 #pragma unroll
             for (int n = 0; n < C::NB; ++n)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[m][n][e]);
-            bmax[m] = xmax(mx);
-            up |= bmax[m] > mrun[m] + kSlack;
+                for (int e = 0; e < 4; ++e) mx = fmaxf(mx, !MASK || 16 * n + e < lim ? s[m][n][e] : -INFINITY);
+            lmax[m] = mx;
+            up |= mx != -INFINITY && p.c * mx > mrun[m] + kSlack;
         }
         // The reference maximum of a row moves only when a block's maximum exceeds it
         // by more than kSlack (always in the first block): the probabilities are taken
@@ -336,10 +331,16 @@ struct Attn {
         // that data with a steady maximum skips after the first block.  Any reference
         // gives the same softmax; this one saves the rescale of 128 accumulators per
         // block.
-        if (__builtin_amdgcn_ballot_w64(up)) {
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(up) != 0, 0)) {
+#pragma unroll
+            for (int m = 0; m < C::FM; ++m)
+#pragma unroll
+                for (int n = 0; n < C::DN; ++n) asm volatile("" : "+a"(o[m][n]));
 #pragma unroll
             for (int m = 0; m < C::FM; ++m) {
-                const float mnew = bmax[m] > mrun[m] + kSlack ? bmax[m] : mrun[m];
+                const float mx = xmax(lmax[m]);
+                const float bmax = mx == -INFINITY ? -INFINITY : p.c * mx;  // (c = 0: every logit is 0)
+                const float mnew = bmax > mrun[m] + kSlack ? bmax : mrun[m];
                 const float alpha = __builtin_amdgcn_exp2f(mrun[m] - mnew);  // 0 in the first block
                 mrun[m] = mnew;
                 lrun[m] *= alpha;
@@ -356,7 +357,9 @@ struct Attn {
             for (int n = 0; n < C::NB; ++n)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    x[n][e] = __builtin_amdgcn_exp2f(x[n][e] - mrun[m]);
+#pragma clang fp contract(off)
+                    x[n][e] = __builtin_amdgcn_exp2f(x[n][e] * p.c - mrun[m]);  // (rounded product: no fma)
+                    if (MASK && 16 * n + e >= lim) x[n][e] = 0.f;
                     sum += x[n][e];
                 }
             lrun[m] += sum;
@@ -460,7 +463,7 @@ struct Attn {
             }
             uint32_t rs = 0;                                   // stage of block t
             uint32_t ws = (C::S - 1) * C::STAGE_BYTES;         // stage of block t + S - 1
-            for (int t = 0; t < nb; ++t) {
+            auto step = [&](int t, auto last) {
                 wait_lgkmcnt0();                              // this wave's reads of block t-1 are done
                 wait_vmcnt<(C::S - 2) * C::LOADS>();          // its copies of block t have landed
                 barrier();                                    // block t visible; the stage of t-1 free
@@ -469,10 +472,12 @@ struct Attn {
                 poison(lds0 + ws, wave, lane);
 #endif
                 dma_block(cp, dk, dv, lds0 + ws, wave);       // block t+S-1 into that stage
-                block(p, smem + rs, L, qf, o, mrun, lrun, t, lane, [] {});
+                block<decltype(last)::value>(p, smem + rs, L, qf, o, mrun, lrun, t, lane, [] {});
                 rs = rs + C::STAGE_BYTES == (uint32_t)C::LDS_BYTES ? 0u : rs + C::STAGE_BYTES;
                 ws = ws + C::STAGE_BYTES == (uint32_t)C::LDS_BYTES ? 0u : ws + C::STAGE_BYTES;
-            }
+            };
+            for (int t = 0; t + 1 < nb; ++t) step(t, std::false_type{});  // the last block runs with the mask
+            if (nb > 0) step(nb - 1, std::true_type{});
             wait_vmcnt<0>();  // no copy may still be writing this workgroup's LDS
         } else if constexpr (C::V == V_REG) {
             i32x4_t r[C::LOADS];
@@ -483,30 +488,35 @@ struct Attn {
                 wait_lgkmcnt0();
                 barrier();
             }
-            for (int t = 0; t < nb; ++t) {
+            auto step = [&](int t, auto last) {
                 SPT_LDS char* cur = smem + (C::S == 2 ? (t & 1) : 0) * C::STAGE_BYTES;
                 SPT_LDS char* nxt = smem + (C::S == 2 ? ((t + 1) & 1) : 0) * C::STAGE_BYTES;
                 // block t+1 is fetched while block t is computed: issued once S = Q K^T is
                 // done (before it, the K fragments hold the registers the fetch needs),
                 // in flight over the softmax and O += P V (past the end: zero-length, zeros)
-                block(p, cur, L, qf, o, mrun, lrun, t, lane, [&] { load_block(p, slice, t + 1, cp, r); });
+                block<decltype(last)::value>(p, cur, L, qf, o, mrun, lrun, t, lane,
+                                             [&] { load_block(p, slice, t + 1, cp, r); });
                 if constexpr (C::S == 1) barrier();       // one buffer: every read of it done first
                 wait_vmcnt<0>();
                 store_block(nxt, wave, lane, r);
                 wait_lgkmcnt0();
                 barrier();
-            }
+            };
+            for (int t = 0; t + 1 < nb; ++t) step(t, std::false_type{});
+            if (nb > 0) step(nb - 1, std::true_type{});
         } else {
             i32x4_t r[C::LOADS];
-            for (int t = 0; t < nb; ++t) {  // load -> barrier -> compute -> barrier
+            auto step = [&](int t, auto last) {  // load -> barrier -> compute -> barrier
                 load_block(p, slice, t, cp, r);
                 wait_vmcnt<0>();
                 store_block(smem, wave, lane, r);
                 wait_lgkmcnt0();
                 barrier();
-                block(p, smem, L, qf, o, mrun, lrun, t, lane, [] {});
+                block<decltype(last)::value>(p, smem, L, qf, o, mrun, lrun, t, lane, [] {});
                 barrier();
-            }
+            };
+            for (int t = 0; t + 1 < nb; ++t) step(t, std::false_type{});
+            if (nb > 0) step(nb - 1, std::true_type{});
         }
 
         // O = acc / l for the rows this wave owns inside Sq
