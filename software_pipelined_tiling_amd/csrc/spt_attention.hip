@@ -22,12 +22,15 @@
 // kernel.  For every block of BKV keys (64; 32 with 128 columns, whose
 // accumulators leave fewer registers) a wave computes
 //     S = Q K^T           (16 x v_mfma_f32_16x16x32 per 32-wide d-step),
-//     the online softmax  (a reference row maximum m, the running sum l, and a
-//                          rescale of the output accumulators by 2^(m_old - m_new)
-//                          when m moves),
-//     O += P V            (P rounded to the input type, 16-bit MFMAs),
-// and finally writes O / l in fp32.  Exponentials are base 2 with log2(e)
-// folded into the scale.
+//     the online softmax  (a reference row maximum m and a rescale of the output
+//                          accumulators and row sums by 2^(m_old - m_new) when m
+//                          moves; P = 2^(c S - m), rounded to the input type),
+//     O += P V            (16-bit MFMAs),
+//     l += P 1            (the row sums of the rounded P: one more MFMA per row
+//                          block, against a fragment of ones),
+// and finally writes O / l in fp32: the weights P / l of a row sum to one over
+// the very values the second product used.  Exponentials are base 2 with
+// log2(e) folded into the scale c.
 //
 // MFMA layouts (operands swapped as in the GEMM: the K or V fragment is the
 // first operand).  S block (m, n): lane (g = lane/16, i = lane%16) holds query
@@ -47,7 +50,7 @@
 // at each position; a copy of one wave moves 1 KiB of whole rows.
 //
 // Edges.  Keys past Sk: the last block's descriptor ends at the slice, so its
-// copies read zeros there, and those keys get weight 0 (their logits are -inf).
+// copies read zeros there, and those keys get no maximum and weight 0.
 // Query rows past Sq read zeros and are never stored.
 #include <hip/hip_runtime.h>
 
@@ -252,6 +255,10 @@ struct Attn {
         }
     }
 
+    // A fragment of ones in the input type: P against it gives P's row sums.
+    static constexpr int kOneWord = C::DT == DT_F16 ? 0x3C003C00 : 0x3F803F80;
+    static constexpr i32x4_t kOnes = {kOneWord, kOneWord, kOneWord, kOneWord};
+
     // Two probabilities -> one 32-bit word of the input type (round to nearest even).
     static __device__ __forceinline__ int pack2(float a, float b)
     {
@@ -269,118 +276,145 @@ struct Attn {
         v = fmaxf(v, __shfl_xor(v, 16));
         return fmaxf(v, __shfl_xor(v, 32));
     }
-    static __device__ __forceinline__ float xsum(float v)
-    {
-        v += __shfl_xor(v, 16);
-        return v + __shfl_xor(v, 32);
-    }
 
-    // One key block from the stage at `st`: S = Q K^T, online softmax, O += P V.
-    // `mid` runs between S = Q K^T and the softmax, once the K fragments are dead.
+
+    // One key block from the stage at `st`: S = Q K^T, online softmax, O += P V, by
+    // 16-row query blocks m, so that the vector-ALU work of one row block's softmax is
+    // issued between the MFMAs of the next (with one wave per SIMD, the wave issues
+    // the next few instructions while an MFMA runs; a softmax issued alone leaves the
+    // matrix pipe idle):
+    //     S(0);  S(1) | sm(0);  S(2) | sm(1);  S(3) | sm(2);  PV(0) | sm(3);  PV(1..3)
+    // S(m): the 8 MFMAs of row block m's scores (the block's K fragments are all read
+    // first); sm(m): its softmax in 8 pieces, one after each MFMA of the group; PV(m):
+    // the 8 MFMAs of O(m) += P(m) V (the V fragments are all read during S(3)).  `mid`
+    // runs once every K fragment is dead.
+    //
+    // The scores stay unscaled until the exponent: the test compares c max S (c >= 0)
+    // with the row's reference, and each probability is 2^(c S - m) with one fma (at
+    // the row maximum, 2 to the rounding residue of c S, which rounds to 1 in the
+    // input type for logits below 2^10 in magnitude).  Each lane tests its own
+    // logits: a row needs a new reference when one of them exceeds it by more than
+    // kSlack, which the wave learns from one ballot per row block; only then are the
+    // row maxima reduced across the row's four lanes, the row's output and sum rescaled
+    // by 2^(old - new), and its probabilities taken again.  Any reference gives the
+    // same softmax; this one keeps the probabilities below 2^kSlack and spares the
+    // accumulators a rescale on every block.  MASK (the last block): keys past Sk get
+    // no maximum and weight 0.
     template <bool MASK, class F>
     static __device__ __forceinline__ void block(const AttnArgs& p, const SPT_LDS char* st, const Lanes& L,
                                                  const i32x4_t (&qf)[C::FM][C::KS], acc_t (&o)[C::FM][C::DN],
-                                                 float (&mrun)[C::FM], float (&lrun)[C::FM], int t, int lane, F&& mid)
+                                                 float (&mrun)[C::FM], acc_t (&lacc)[C::FM], int t, int lane, F&& mid)
     {
+        constexpr int NK = C::KS * C::NB;  // K fragment f: d-step f / NB, key block f % NB
+        constexpr int NF = C::US * C::DN;  // V fragment f: key-step f / DN, column block f % DN
+        constexpr int E = 4 * C::NB;       // scores of one row block per lane: key 16 (e / 4) + e % 4
+        static_assert(NK == 8 && NF == 8 && C::FM == 4, "4 row blocks of 8 MFMAs in both products");
+        const int lim = p.Sk - t * C::BKV - 4 * (lane >> 4);  // keys 16 n + e < lim are inside Sk
+
+        i32x4_t kf[NK], vf[NF];
+        static_for<0, NK>([&](auto fc) {
+            constexpr int f = decltype(fc)::value;
+            kf[f] = read_k(st, L, f % C::NB, f / C::NB);
+        });
         acc_t s[C::FM][C::NB];
 #pragma unroll
         for (int m = 0; m < C::FM; ++m)
 #pragma unroll
             for (int n = 0; n < C::NB; ++n) s[m][n] = (acc_t){0, 0, 0, 0};
-        // S = Q K^T over the (d-step, key block) fragments in order, each read two
-        // fragments ahead of its MFMAs
-        constexpr int NK = C::KS * C::NB;
-        i32x4_t kf[3];
-        kf[0] = read_k(st, L, 0, 0);
-        kf[1] = read_k(st, L, 1 % C::NB, 1 / C::NB);
-        static_for<0, NK>([&](auto fc) {
-            constexpr int f = decltype(fc)::value;
-            if constexpr (f + 2 < NK) kf[(f + 2) % 3] = read_k(st, L, (f + 2) % C::NB, (f + 2) / C::NB);
-#pragma unroll
-            for (int m = 0; m < C::FM; ++m) mma<C::DT>(s[m][f % C::NB], kf[f % 3], qf[m][f / C::NB]);
-        });
+        i32x4_t pf[C::FM][C::US];
+        float lmax[C::FM], pe[C::FM][E];
+        bool up[C::FM];
 
-        mid();
-
-        // The scores stay unscaled until the exponent: the test below compares c max S
-        // (c >= 0; rounding is monotonic, so that is the largest rounded logit c S) with
-        // the reference, and each probability is 2^(x - m) with x = c S rounded first, so
-        // that the logit equal to the reference gives exactly 1.  MASK (the last block):
-        // keys past Sk get no maximum and weight 0.
-        const int lim = p.Sk - t * C::BKV - 4 * (lane >> 4);  // keys 16 n + e < lim are inside Sk
-        // Each lane tests its own logits against the reference: a row needs a new one
-        // when any of its logits exceeds the reference by more than kSlack, which the
-        // wave learns from one ballot; only then are the row maxima reduced across the
-        // row's four lanes.
-        float lmax[C::FM];
-        bool up = false;
+        // piece j (0 .. 7) of the softmax of row block m: the lane's maximum (0, 1) and
+        // the test (1), the probabilities and their sum (2 .. 5), packing (6, 7)
+        auto sm = [&](auto mc, auto jc) {
+            constexpr int m = decltype(mc)::value, j = decltype(jc)::value;
+            const auto sc = [&](int e) { return s[m][e / 4][e % 4]; };
+            const auto valid = [&](int e) { return !MASK || 16 * (e / 4) + e % 4 < lim; };
+            if constexpr (j == 0) {
+                float mx = -INFINITY;
 #pragma unroll
-        for (int m = 0; m < C::FM; ++m) {
-            float mx = -INFINITY;
+                for (int e = 0; e < E / 2; ++e) mx = fmaxf(mx, valid(e) ? sc(e) : -INFINITY);
+                lmax[m] = mx;
+            } else if constexpr (j == 1) {
+                float mx = lmax[m];
 #pragma unroll
-            for (int n = 0; n < C::NB; ++n)
+                for (int e = E / 2; e < E; ++e) mx = fmaxf(mx, valid(e) ? sc(e) : -INFINITY);
+                lmax[m] = mx;
+                up[m] = mx != -INFINITY && p.c * mx > mrun[m] + kSlack;
+            } else if constexpr (j <= 5) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) mx = fmaxf(mx, !MASK || 16 * n + e < lim ? s[m][n][e] : -INFINITY);
-            lmax[m] = mx;
-            up |= mx != -INFINITY && p.c * mx > mrun[m] + kSlack;
-        }
-        // The reference maximum of a row moves only when a block's maximum exceeds it
-        // by more than kSlack (always in the first block): the probabilities are taken
-        // relative to the reference, so they stay below 2^kSlack, and the output rows
-        // and sums are rescaled by 2^(old - new) only then -- a wave-uniform branch
-        // that data with a steady maximum skips after the first block.  Any reference
-        // gives the same softmax; this one saves the rescale of 128 accumulators per
-        // block.
-        if (__builtin_expect(__builtin_amdgcn_ballot_w64(up) != 0, 0)) {
-#pragma unroll
-            for (int m = 0; m < C::FM; ++m)
+                for (int e = (j - 2) * E / 4; e < (j - 1) * E / 4; ++e) {
+                    const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(sc(e), p.c, -mrun[m]));
+                    pe[m][e] = valid(e) ? v : 0.f;
+                    // (an empty use, so that the compiler does not sink this work past the
+                    // ballot's branch, out of the MFMA group it is meant to overlap)
+                    asm volatile("" ::"v"(pe[m][e]));
+                }
+            } else if constexpr (j - 6 < C::US) {
+                constexpr int u = j - 6;
+                const float* x = pe[m] + 8 * u;
+                pf[m][u] = (i32x4_t){pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
+                asm volatile("" ::"v"(pf[m][u]));
+            }
+        };
+        // after sm(m): a new reference where the ballot asks for one
+        auto settle = [&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            if (__builtin_expect(__builtin_amdgcn_ballot_w64(up[m]) != 0, 0)) {
+                // (the accumulators live in AGPRs: the pin keeps their VGPR copies for the
+                // multiply inside this branch)
 #pragma unroll
                 for (int n = 0; n < C::DN; ++n) asm volatile("" : "+a"(o[m][n]));
-#pragma unroll
-            for (int m = 0; m < C::FM; ++m) {
+                asm volatile("" : "+a"(lacc[m]));
                 const float mx = xmax(lmax[m]);
                 const float bmax = mx == -INFINITY ? -INFINITY : p.c * mx;  // (c = 0: every logit is 0)
                 const float mnew = bmax > mrun[m] + kSlack ? bmax : mrun[m];
                 const float alpha = __builtin_amdgcn_exp2f(mrun[m] - mnew);  // 0 in the first block
                 mrun[m] = mnew;
-                lrun[m] *= alpha;
+                lacc[m] *= alpha;
 #pragma unroll
                 for (int n = 0; n < C::DN; ++n) o[m][n] *= alpha;
+                static_for<2, 8>([&](auto jc) { sm(mc, jc); });  // the probabilities again
             }
-        }
-        i32x4_t pf[C::FM][C::US];
-#pragma unroll
-        for (int m = 0; m < C::FM; ++m) {
-            acc_t (&x)[C::NB] = s[m];
-            float sum = 0.f;
-#pragma unroll
-            for (int n = 0; n < C::NB; ++n)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-#pragma clang fp contract(off)
-                    x[n][e] = __builtin_amdgcn_exp2f(x[n][e] * p.c - mrun[m]);  // (rounded product: no fma)
-                    if (MASK && 16 * n + e >= lim) x[n][e] = 0.f;
-                    sum += x[n][e];
-                }
-            lrun[m] += sum;
-#pragma unroll
-            for (int u = 0; u < C::US; ++u)
-                pf[m][u] = (i32x4_t){pack2(x[2 * u][0], x[2 * u][1]), pack2(x[2 * u][2], x[2 * u][3]),
-                                     pack2(x[2 * u + 1][0], x[2 * u + 1][1]), pack2(x[2 * u + 1][2], x[2 * u + 1][3])};
-        }
-
-        // O += P V over the (key-step, column block) fragments in order, each read
-        // two fragments ahead of its MFMAs
-        constexpr int NF = C::US * C::DN;
-        i32x4_t vf[3];
-        vf[0] = read_v(st, L, 0, 0);
-        vf[1] = read_v(st, L, 1 % C::DN, 1 / C::DN);
-        static_for<0, NF>([&](auto fc) {
-            constexpr int f = decltype(fc)::value;
-            if constexpr (f + 2 < NF) vf[(f + 2) % 3] = read_v(st, L, (f + 2) % C::DN, (f + 2) / C::DN);
-#pragma unroll
-            for (int m = 0; m < C::FM; ++m) mma<C::DT>(o[m][f % C::DN], vf[f % 3], pf[m][f / C::DN]);
-        });
+        };
+        // group: the 8 MFMAs of S(m) (PV = false) or PV(m), piece j of sm(k) after MFMA j
+        // (k < 0: none), the V fragments read after the MFMAs of S(3)
+        auto group = [&](auto mc, auto pvc, auto kc) {
+            constexpr int m = decltype(mc)::value, k = decltype(kc)::value;
+            constexpr bool PV = decltype(pvc)::value;
+            static_for<0, 8>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                if constexpr (PV)
+                    mma<C::DT>(o[m][j % C::DN], vf[j], pf[m][j / C::DN]);
+                else
+                    mma<C::DT>(s[m][j % C::NB], kf[j], qf[m][j / C::NB]);
+                if constexpr (k >= 0) sm(std::integral_constant<int, k>{}, jc);
+                if constexpr (!PV && m == C::FM - 1) vf[j] = read_v(st, L, j % C::DN, j / C::DN);
+                order_fence();
+            });
+            // PV(m) also takes the row sums of P(m): an MFMA against a fragment of ones
+            if constexpr (PV)
+                static_for<0, C::US>([&](auto uc) { mma<C::DT>(lacc[m], kOnes, pf[m][decltype(uc)::value]); });
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        using I3 = std::integral_constant<int, 3>;
+        using NONE = std::integral_constant<int, -1>;
+        group(I0{}, std::false_type{}, NONE{});
+        group(I1{}, std::false_type{}, I0{});
+        settle(I0{});
+        group(I2{}, std::false_type{}, I1{});
+        settle(I1{});
+        group(I3{}, std::false_type{}, I2{});
+        settle(I2{});
+        mid();
+        group(I0{}, std::true_type{}, I3{});
+        settle(I3{});
+        group(I1{}, std::true_type{}, NONE{});
+        group(I2{}, std::true_type{}, NONE{});
+        group(I3{}, std::true_type{}, NONE{});
     }
 
     // XCD-aware placement: workgroups are dispatched round-robin over the 8 XCDs;
@@ -440,11 +474,12 @@ struct Attn {
         setup_lanes(lane, L);
 
         acc_t o[C::FM][C::DN];
-        float mrun[C::FM], lrun[C::FM];
+        float mrun[C::FM];
+        acc_t lacc[C::FM];  // row sums of the probabilities: every element of lane (g, i) holds row i's
 #pragma unroll
         for (int m = 0; m < C::FM; ++m) {
             mrun[m] = -INFINITY;
-            lrun[m] = 0.f;
+            lacc[m] = (acc_t){0, 0, 0, 0};
 #pragma unroll
             for (int n = 0; n < C::DN; ++n) o[m][n] = (acc_t){0, 0, 0, 0};
         }
@@ -472,7 +507,7 @@ struct Attn {
                 poison(lds0 + ws, wave, lane);
 #endif
                 dma_block(cp, dk, dv, lds0 + ws, wave);       // block t+S-1 into that stage
-                block<decltype(last)::value>(p, smem + rs, L, qf, o, mrun, lrun, t, lane, [] {});
+                block<decltype(last)::value>(p, smem + rs, L, qf, o, mrun, lacc, t, lane, [] {});
                 rs = rs + C::STAGE_BYTES == (uint32_t)C::LDS_BYTES ? 0u : rs + C::STAGE_BYTES;
                 ws = ws + C::STAGE_BYTES == (uint32_t)C::LDS_BYTES ? 0u : ws + C::STAGE_BYTES;
             };
@@ -494,7 +529,7 @@ struct Attn {
                 // block t+1 is fetched while block t is computed: issued once S = Q K^T is
                 // done (before it, the K fragments hold the registers the fetch needs),
                 // in flight over the softmax and O += P V (past the end: zero-length, zeros)
-                block<decltype(last)::value>(p, cur, L, qf, o, mrun, lrun, t, lane,
+                block<decltype(last)::value>(p, cur, L, qf, o, mrun, lacc, t, lane,
                                              [&] { load_block(p, slice, t + 1, cp, r); });
                 if constexpr (C::S == 1) barrier();       // one buffer: every read of it done first
                 wait_vmcnt<0>();
@@ -512,7 +547,7 @@ struct Attn {
                 store_block(smem, wave, lane, r);
                 wait_lgkmcnt0();
                 barrier();
-                block<decltype(last)::value>(p, smem, L, qf, o, mrun, lrun, t, lane, [] {});
+                block<decltype(last)::value>(p, smem, L, qf, o, mrun, lacc, t, lane, [] {});
                 barrier();
             };
             for (int t = 0; t + 1 < nb; ++t) step(t, std::false_type{});
@@ -522,12 +557,14 @@ struct Attn {
         // O = acc / l for the rows this wave owns inside Sq
 #pragma unroll
         for (int m = 0; m < C::FM; ++m) {
-            const float inv = 1.0f / xsum(lrun[m]);
+            const float l = lacc[m][0];
             const int q = qw + 16 * m + i;
             if (q < p.Sq) {
+                // (a correctly rounded division, not a product with 1 / l: where every value
+                // row is the same power of two, O is that value exactly)
                 char* row = p.O + ((long long)slice * p.Sq + q) * (C::D * 4);
 #pragma unroll
-                for (int n = 0; n < C::DN; ++n) *(acc_t*)(row + (16 * n + 4 * g) * 4) = o[m][n] * inv;
+                for (int n = 0; n < C::DN; ++n) *(acc_t*)(row + (16 * n + 4 * g) * 4) = o[m][n] / l;
             }
         }
     }

@@ -318,10 +318,11 @@ class AttnKernel:
 
     @property
     def geometry(self):
-        """Per key block: BKV keys, MFMAs per wave (S = Q K^T, then O += P V over the
-        wave's 64 query rows), 16-byte copies per thread, stage bytes (K and V blocks)."""
+        """Per key block: BKV keys, MFMAs per wave (S = Q K^T, O += P V and the row sums
+        of P over the wave's 64 query rows), 16-byte copies per thread, stage bytes (K
+        and V blocks)."""
         bkv = 32 if self.D == 128 else 64
-        mfma = 4 * (bkv // 16) * (self.D // 32) + 4 * (self.D // 16) * (bkv // 32)
+        mfma = 4 * (bkv // 16) * (self.D // 32) + 4 * (self.D // 16) * (bkv // 32) + 4 * (bkv // 32)
         loads = 2 * (bkv * self.D * 2) // 16 // 256
         return dict(bkv=bkv, mfma_per_block=mfma, loads_per_block=loads, stage_bytes=2 * bkv * self.D * 2)
 

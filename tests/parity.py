@@ -84,9 +84,11 @@ def sample_entries(M: int, N: int, n: int, rng: np.random.Generator, BM: int = 1
 
 # Attention: O_gpu - O_ref at (b, i, d), over max_j |V[b, j, d]|.  The softmax weights of a
 # row sum to one, so |O[b, i, d]| <= max_j |V[b, j, d]|: this is the scale of every output
-# in column d.  Rounding the probabilities to the input type before the second product
-# perturbs each by at most 2^-8 (bf16) or 2^-11 (fp16) relatively, hence the output by
-# at most that times max_j |V[b, j, d]|; fp32 sums add far less.
+# in column d.  The kernel rounds each probability to the input type (relative error at
+# most u = 2^-8 for bf16, 2^-11 for fp16) and divides by the sum of the rounded values,
+# so its weights are w_j (1 + e_j) / (1 + sum_k w_k e_k): the output moves by
+# sum_j w_j e_j (V_j - O) / (1 + ...), at most 2u / (1 - u) times max_j |V[b, j, d]|
+# (7.84e-3 for bf16, 9.8e-4 for fp16); fp32 sums add far less.
 TOL_ATTN = {"f16": 2e-3, "bf16": 8e-3}
 
 

@@ -92,6 +92,21 @@ def test_one_key_gives_its_value_row(D, variant, stages):
     assert np.array_equal(O, np.broadcast_to(want, O.shape).astype(np.float32))
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_equal_value_rows_give_that_value_exactly(dtype, D):
+    """Every value row 0.5: the row sums come from the same rounded probabilities as
+    O += P V (an MFMA against ones), each product with 0.5 is exact and so is every
+    partial sum's halving, so O = l / 2 / l = 0.5 exactly, for every producer, a ragged
+    last block and any logits."""
+    Q, K, V = qkv(dtype, 2, 70, 333, D, 74)
+    half = I.f64_to_f16_bits(np.full((1,), 0.5))[0] if dtype == "f16" else I.f32_to_bf16_bits(np.full((1,), 0.5, np.float32))[0]
+    V = np.full_like(V, half)
+    for variant, stages in VARIANTS:
+        O = run(Q, K, V, dtype, 0.3, variant, stages)
+        assert np.array_equal(O, np.full(O.shape, 0.5, np.float32)), (variant, stages)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("Sk", [64, 100, 1000])
 def test_selection_by_huge_logits(D, Sk):
