@@ -152,11 +152,13 @@ def time_calls(prob: Problem, steps: int, warmup: int, variant="auto", stages=0,
     return e0.elapsed_time(e1) / steps
 
 
-def time_graph(fn, calls: int = 20, reps: int = 10):
+def time_graph(fn, calls: int = 20, reps: int = 10, settle_s: float = 0.02):
     """Microseconds per call of `fn(stream_handle)` with `calls` calls captured in one
-    HIP graph and the graph replayed `reps` times between two events (after one
-    untimed replay): the GPU time of back-to-back calls, host launch cost excluded
-    (short kernels launched one by one from Python would wait on the host)."""
+    HIP graph: the graph is replayed untimed for `settle_s` seconds (the clock settles
+    after the previous workload), then `reps` times with an event pair around each
+    replay; the median replay over `calls`.  This is the GPU time of back-to-back
+    calls, host launch cost excluded (short kernels launched one by one from Python
+    would wait on the host)."""
     import torch
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
@@ -169,17 +171,22 @@ def time_graph(fn, calls: int = 20, reps: int = 10):
             for _ in range(calls):
                 fn(torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    stream = torch.cuda.current_stream()
-    e0.record(stream)
-    for _ in range(reps):
+    t0 = time.perf_counter()
+    n = 0
+    while n < 1 or time.perf_counter() - t0 < settle_s:
         g.replay()
-    e1.record(stream)
+        torch.cuda.synchronize()
+        n += 1
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
     torch.cuda.synchronize()
     del g
-    return e0.elapsed_time(e1) / (reps * calls) * 1e3
+    per = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    return per[len(per) // 2] / calls * 1e3
 
 
 def gemm_us(prob: Problem, variant="auto", stages=0, tile=0, K=None):
@@ -673,8 +680,9 @@ def main():
                     extra[wk.name]["value_over_ceiling"] = round(tf / ceil, 4)
             del p
         out["workloads"] = extra
-        out["workloads_timing"] = ("every side workload: 20 calls captured in one HIP graph, replayed 10 times "
-                                   "between two events after one untimed replay (GPU time of back-to-back calls)")
+        out["workloads_timing"] = ("every side workload: 20 calls captured in one HIP graph, replayed untimed for "
+                                   "20 ms, then 10 times with an event pair around each replay; the median replay "
+                                   "over 20 (GPU time of back-to-back calls)")
 
         if not args.only_workload and not args.only_attention:
             out["streaming"] = stream_bench(steps, 20)
