@@ -17,10 +17,11 @@
 //            just freed -> compute block t ("Hiding Memory Latency in CUDA:
 //            Asynchronous Loads and Software Pipelines", sections 3-5).
 //
-// One workgroup of 4 waves owns 256 query rows of one (batch, head) slice;
-// each wave owns 64 rows, whose Q fragments stay in registers for the whole
-// kernel.  For every block of BKV keys (64; 32 with 128 columns, whose
-// accumulators leave fewer registers) a wave computes
+// One workgroup of 8 waves (two per SIMD, so that one wave's scalar, LDS and
+// wait instructions issue beside the other's vector work) owns 256 query rows
+// of one (batch, head) slice; each wave owns 32 rows, whose Q fragments stay in
+// registers for the whole kernel.  For every block of BKV keys (64; 32 with 128
+// columns, whose accumulators leave fewer registers) a wave computes
 //     S = Q K^T           (16 x v_mfma_f32_16x16x32 per 32-wide d-step),
 //     the online softmax  (a reference row maximum m and a rescale of the output
 //                          accumulators and row sums by 2^(m_old - m_new) when m
@@ -75,8 +76,8 @@ struct AttnArgs {
 template <int DT_, int D_, int V_, int S_>
 struct AttnCfg {
     static constexpr int DT = DT_, D = D_, V = V_, S = S_;
-    static constexpr int WAVES = 4, THREADS = 256;
-    static constexpr int WQ = 64, BQ = WAVES * WQ;  // query rows per wave / per workgroup
+    static constexpr int WAVES = 8, THREADS = 64 * WAVES;  // two waves per SIMD
+    static constexpr int WQ = 32, BQ = WAVES * WQ;  // query rows per wave / per workgroup
     static constexpr int BKV = D_ == 128 ? 32 : 64;  // keys per block (128 columns: 32, for registers)
     static constexpr int FM = WQ / 16;              // 16-row query blocks per wave
     static constexpr int NB = BKV / 16;             // 16-key blocks per key block
@@ -279,15 +280,15 @@ struct Attn {
 
 
     // One key block from the stage at `st`: S = Q K^T, online softmax, O += P V, by
-    // 16-row query blocks m, so that the vector-ALU work of one row block's softmax is
-    // issued between the MFMAs of the next (with one wave per SIMD, the wave issues
-    // the next few instructions while an MFMA runs; a softmax issued alone leaves the
-    // matrix pipe idle):
-    //     S(0);  S(1) | sm(0);  S(2) | sm(1);  S(3) | sm(2);  PV(0) | sm(3);  PV(1..3)
+    // 16-row query blocks m (FM of them), so that the vector-ALU work of one row
+    // block's softmax is issued between the MFMAs of the next (a wave issues the next
+    // few instructions while an MFMA runs; a softmax issued alone leaves the matrix
+    // pipe idle):
+    //     S(0);  S(m) | sm(m-1) for m = 1 .. FM-1;  PV(0) | sm(FM-1);  PV(1 .. FM-1)
     // S(m): the 8 MFMAs of row block m's scores (the block's K fragments are all read
     // first); sm(m): its softmax in 8 pieces, one after each MFMA of the group; PV(m):
-    // the 8 MFMAs of O(m) += P(m) V (the V fragments are all read during S(3)).  `mid`
-    // runs once every K fragment is dead.
+    // the 8 MFMAs of O(m) += P(m) V (the V fragments are all read during the last S
+    // group).  `mid` runs once every K fragment is dead.
     //
     // The scores stay unscaled until the exponent: the test compares c max S (c >= 0)
     // with the row's reference, and each probability is 2^(c S - m) with one fma (at
@@ -308,7 +309,7 @@ struct Attn {
         constexpr int NK = C::KS * C::NB;  // K fragment f: d-step f / NB, key block f % NB
         constexpr int NF = C::US * C::DN;  // V fragment f: key-step f / DN, column block f % DN
         constexpr int E = 4 * C::NB;       // scores of one row block per lane: key 16 (e / 4) + e % 4
-        static_assert(NK == 8 && NF == 8 && C::FM == 4, "4 row blocks of 8 MFMAs in both products");
+        static_assert(NK == 8 && NF == 8, "8 MFMAs per row block in both products");
         const int lim = p.Sk - t * C::BKV - 4 * (lane >> 4);  // keys 16 n + e < lim are inside Sk
 
         i32x4_t kf[NK], vf[NF];
@@ -379,7 +380,7 @@ struct Attn {
             }
         };
         // group: the 8 MFMAs of S(m) (PV = false) or PV(m), piece j of sm(k) after MFMA j
-        // (k < 0: none), the V fragments read after the MFMAs of S(3)
+        // (k < 0: none), the V fragments read beside the MFMAs of the last S group
         auto group = [&](auto mc, auto pvc, auto kc) {
             constexpr int m = decltype(mc)::value, k = decltype(kc)::value;
             constexpr bool PV = decltype(pvc)::value;
@@ -397,24 +398,16 @@ struct Attn {
             if constexpr (PV)
                 static_for<0, C::US>([&](auto uc) { mma<C::DT>(lacc[m], kOnes, pf[m][decltype(uc)::value]); });
         };
-        using I0 = std::integral_constant<int, 0>;
-        using I1 = std::integral_constant<int, 1>;
-        using I2 = std::integral_constant<int, 2>;
-        using I3 = std::integral_constant<int, 3>;
-        using NONE = std::integral_constant<int, -1>;
-        group(I0{}, std::false_type{}, NONE{});
-        group(I1{}, std::false_type{}, I0{});
-        settle(I0{});
-        group(I2{}, std::false_type{}, I1{});
-        settle(I1{});
-        group(I3{}, std::false_type{}, I2{});
-        settle(I2{});
+        // S(0); S(m) | sm(m-1) for m = 1 .. FM-1; PV(0) | sm(FM-1); PV(m) for m = 1 .. FM-1
+        static_for<0, C::FM>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            group(mc, std::false_type{}, std::integral_constant<int, m - 1>{});
+            if constexpr (m >= 1) settle(std::integral_constant<int, m - 1>{});
+        });
         mid();
-        group(I0{}, std::true_type{}, I3{});
-        settle(I3{});
-        group(I1{}, std::true_type{}, NONE{});
-        group(I2{}, std::true_type{}, NONE{});
-        group(I3{}, std::true_type{}, NONE{});
+        group(std::integral_constant<int, 0>{}, std::true_type{}, std::integral_constant<int, C::FM - 1>{});
+        settle(std::integral_constant<int, C::FM - 1>{});
+        static_for<1, C::FM>([&](auto mc) { group(mc, std::true_type{}, std::integral_constant<int, -1>{}); });
     }
 
     // XCD-aware placement: workgroups are dispatched round-robin over the 8 XCDs;
@@ -571,7 +564,8 @@ struct Attn {
 };
 
 template <class C>
-__global__ __attribute__((amdgpu_flat_work_group_size(C::THREADS, C::THREADS), amdgpu_waves_per_eu(1, 1))) void
+__global__ __attribute__((amdgpu_flat_work_group_size(C::THREADS, C::THREADS),
+                          amdgpu_waves_per_eu(C::WAVES / 4, C::WAVES / 4))) void
 attention_kernel(AttnArgs p)
 {
     Attn<C>::run(p);

@@ -322,8 +322,9 @@ class AttnKernel:
         of P over the wave's 64 query rows), 16-byte copies per thread, stage bytes (K
         and V blocks)."""
         bkv = 32 if self.D == 128 else 64
-        mfma = 4 * (bkv // 16) * (self.D // 32) + 4 * (self.D // 16) * (bkv // 32) + 4 * (bkv // 32)
-        loads = 2 * (bkv * self.D * 2) // 16 // 256
+        fm = 2  # 16-row query blocks per wave (32 rows; 8 waves, two per SIMD)
+        mfma = fm * (bkv // 16) * (self.D // 32) + fm * (self.D // 16) * (bkv // 32) + fm * (bkv // 32)
+        loads = 2 * (bkv * self.D * 2) // 16 // 512
         return dict(bkv=bkv, mfma_per_block=mfma, loads_per_block=loads, stage_bytes=2 * bkv * self.D * 2)
 
 

@@ -456,6 +456,22 @@ def test_row_band_full(oracle_mod, dtype, b_col, K):
     assert np.array_equal(C.view(np.uint32), C1.view(np.uint32))
 
 
+@pytest.mark.parametrize("dtype,b_col,K", [("i8", True, 8192), ("f32", False, 2048), ("bf16", True, 4096)])
+def test_row_band_four_stages(oracle_mod, dtype, b_col, K):
+    """A band of at most one workgroup per CU with at least 8 KiB of K per row runs a
+    4-stage ring, for every element type (4224 x 4000: 32 workgroups of 128 x 128 in the
+    band): every output against the oracle (int8 bit-exact), bit-identical to the
+    one-grid 128 x 256 kernel."""
+    M, N = 4224, 4000
+    rc, pi = spt.spt_plan(spt.DTYPE_CODES[dtype], M, N, K, spt.COL if b_col else spt.ROW)
+    assert rc == 0 and pi.band_tile == spt.TILE_128x128 and pi.band_stages == 4 and pi.band_grid == 32
+    A, B = operands(dtype, b_col, M, N, K, 44)
+    C = run(A, B, dtype, b_col, M, N, K)
+    parity.check_full(C, ref(oracle_mod, A, B, dtype, b_col, N, K), A, B, dtype, b_col, M, N, K)
+    C1 = run(A, B, dtype, b_col, M, N, K, "direct", 3, 1)
+    assert np.array_equal(C.view(np.uint32), C1.view(np.uint32))
+
+
 @pytest.mark.parametrize("w", [I.Workload("fp16 GEMM 4100x4104x4104", 41, "f16", 4100, 4104, 4104),
                                I.Workload("int8 GEMM 4100x4112x4112, B column-major", 42, "i8", 4100, 4112, 4112,
                                           True),
