@@ -101,8 +101,11 @@ enum spt_layout { SPT_ROW = 0, SPT_COL = 1 };
  * Valid (variant, stages) pairs: SYNC x 1, REG x {1,2}, DIRECT x {2,3,4},
  * PERSIST x {2,3,4};
  * a ring of S stages must fit in the 160 KiB of LDS (SPT_ERR_UNSUPPORTED
- * otherwise).  stages = 0 picks the variant's default (SYNC 1, REG 2,
- * DIRECT 2 for tiles with a 128-byte K depth, else 3; PERSIST 3).
+ * otherwise), except that DIRECT x 3 on the 256 x 256 x 128-byte tiles
+ * (SPT_TILE_256x256, SPT_TILE_256x256_4W) runs as 5 half-stage slots of
+ * 32 KiB (spt_plan_info.half_stage_slots).  stages = 0 picks the variant's
+ * default (SYNC 1, REG 2, DIRECT 2 for tiles with a 128-byte K depth, else 3;
+ * PERSIST 3).
  */
 enum spt_variant {
     SPT_VARIANT_AUTO = 0,
@@ -170,7 +173,8 @@ typedef struct spt_plan_info {
     int32_t a_stage_bytes;          /* BM*BK*elt */
     int32_t b_stage_bytes;          /* BK*BN*elt */
     int32_t stage_bytes;            /* a + b */
-    int32_t lds_bytes;              /* stages * stage_bytes (LDS per workgroup) */
+    int32_t lds_bytes;              /* stages * stage_bytes (LDS per workgroup; half_stage_slots *
+                                       a_stage_bytes for a half-stage ring) */
     int32_t a_copies_per_thread;    /* 16-byte accesses per thread per stage */
     int32_t b_copies_per_thread;
     int32_t wg_per_cu_lds;          /* floor(163840 / lds_bytes): the LDS limit per CU */
@@ -267,7 +271,8 @@ int spt_scale_by_two(int64_t n, const void* x, void* y, int stages, int blocks, 
  * with 1 stage, SPT_VARIANT_REG with 1-2, SPT_VARIANT_DIRECT with 2-3;
  * SPT_VARIANT_AUTO / stages 0 = the library's choice), the online softmax
  * runs in fp32, and the probabilities are rounded to the input type for the
- * second product.
+ * second product; each row is divided by the sum of those rounded
+ * probabilities.
  *
  * dtype SPT_F16 or SPT_BF16 for Q, K, V; O is fp32.  D (head dimension) is 64
  * or 128.  Layouts (contiguous, DEVICE pointers owned by the caller, 16-byte
