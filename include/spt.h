@@ -126,9 +126,13 @@ enum spt_variant {
  *  SPT_TILE_128x128  128 x 128, 64-byte K depth, 256 threads (2 x 2 waves
  *                    of 64 x 64).
  *  SPT_TILE_256x256_4W  256 x 256, 128-byte K depth, 256 threads (2 x 2
- *                    waves of 128 x 128, one wave per SIMD).
+ *                    waves of 128 x 128, one wave per SIMD).  AUTO picks it
+ *                    for exact-fit shapes only; requested for other shapes,
+ *                    or with the SYNC / REG producers, it runs forms that
+ *                    spill registers (correct, but several times slower).
  *  SPT_TILE_256x256_4W_K64B  the same with a 64-byte K depth (room for a
- *                    3- or 4-stage ring).
+ *                    3- or 4-stage ring; its int8 3- and 4-stage rings spill
+ *                    too, and AUTO never picks them).
  *  SPT_TILE_256x192  256 x 192, 128-byte K depth, 512 threads (2 x 4 waves
  *                    of 128 x 48): fills a round of CUs that the 256 x 256
  *                    grid of a shape would leave partly idle.
