@@ -129,7 +129,7 @@ enum spt_variant {
  *                    waves of 128 x 128, one wave per SIMD).  AUTO picks it
  *                    for exact-fit shapes only; requested for other shapes,
  *                    or with the SYNC / REG producers, it runs forms that
- *                    spill registers (correct, but several times slower).
+ *                    spill registers (correct, but slower).
  *  SPT_TILE_256x256_4W_K64B  the same with a 64-byte K depth (room for a
  *                    3- or 4-stage ring; its int8 3- and 4-stage rings spill
  *                    too, and AUTO never picks them).
