@@ -22,7 +22,8 @@
 // of one (batch, head) slice; each wave owns 32 rows, whose Q fragments stay in
 // registers for the whole kernel.  For every block of BKV keys (64; 32 with 128
 // columns, whose accumulators leave fewer registers) a wave computes
-//     S = Q K^T           (16 x v_mfma_f32_16x16x32 per 32-wide d-step),
+//     S = Q K^T           (v_mfma_f32_16x16x32, one per 16 x 16 score block and
+//                          32-wide d-step),
 //     the online softmax  (a reference row maximum m and a rescale of the output
 //                          accumulators and row sums by 2^(m_old - m_new) when m
 //                          moves; P = 2^(c S - m), rounded to the input type),
@@ -43,7 +44,7 @@
 // (i/4).  O block (m, n): lane holds query row 16m + i, columns 16n + 4g + 0..3
 // (one 16-byte store).
 //
-// LDS stage: the K block (64 rows of 2D bytes) then the V block.  K rows are
+// LDS stage: the K block (BKV rows of 2D bytes) then the V block.  K rows are
 // read 16 at a time at one 16-byte chunk (ds_read_b128), so chunk c of row r
 // sits at c ^ (r' mod chunks) with r' = r / (rows per 256-byte bank line); V is
 // read by 16 rows x 32 bytes (the transposing reads), so its chunk pairs are
