@@ -80,7 +80,7 @@ def test_persistent_grid_is_the_resident_workgroups(driver, dt, lay, M, N, K, st
 
 
 @pytest.mark.parametrize("variant,stages,tile", [(SYNC, 1, 1), (REG, 2, 1), (DIRECT, 3, 1), (DIRECT, 2, 4),
-                                                 (DIRECT, 4, 3), (AUTO, 0, 0)])
+                                                 (DIRECT, 4, 3), (DIRECT, 3, 4), (DIRECT, 3, 2), (AUTO, 0, 0)])
 @pytest.mark.parametrize("dt,lay,M,N,K", [(F16, 0, 4096, 4096, 4096), (BF16, 0, 4000, 3000, 1000),
                                           (I8, 1, 8192, 8192, 512), (F32, 0, 300, 600, 333),
                                           (F16, 0, 4096, 4096, 0)])
