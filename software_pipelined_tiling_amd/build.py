@@ -25,12 +25,15 @@ HEADERS = ["spt_kernel.hpp", "spt_persist.hpp", "spt_instances.hpp", "spt_regist
 # Packed-fp32 VALU instructions are disabled for all device code (-packed-fp32-ops).
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-command-line-argument"]
+# The attention kernel keeps its MFMA results in ordinary VGPRs, where its softmax
+# works on them; the GEMM kernels' 256 accumulators per lane need the AGPRs.
+SOURCE_FLAGS = {"spt_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, defines=(), tag: str = "") -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
-    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src),
-           "-o", obj]
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), *[f"-D{d}" for d in defines], "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-4000:]}")
@@ -134,7 +137,8 @@ def asm(src: str = "spt_kernels_f16_row.hip", out: str | None = None) -> str:
     """gfx950 assembly of one kernel translation unit (for the ISA checks)."""
     os.makedirs(BUILD, exist_ok=True)
     out = out or os.path.join(BUILD, os.path.splitext(src)[0] + ".s")
-    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), "--cuda-device-only", "-S",
+           os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stderr[-4000:]}")

@@ -54,6 +54,12 @@
 // Edges.  Keys past Sk: the last block's descriptor ends at the slice, so its
 // copies read zeros there, and those keys get no maximum and weight 0.
 // Query rows past Sq read zeros and are never stored.
+//
+// Registers.  This unit is built with every MFMA in its VGPR form (the build
+// passes -amdgpu-mfma-vgpr-form to the compiler): the softmax reads the scores
+// and the rare rescale multiplies the output accumulators where the vector ALU
+// can reach them, with no accumulator-register copies, and the whole kernel
+// still fits the 256 registers per lane that two waves per SIMD leave.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -364,11 +370,6 @@ struct Attn {
         auto settle = [&](auto mc) {
             constexpr int m = decltype(mc)::value;
             if (__builtin_expect(__builtin_amdgcn_ballot_w64(up[m]) != 0, 0)) {
-                // (the accumulators live in AGPRs: the pin keeps their VGPR copies for the
-                // multiply inside this branch)
-#pragma unroll
-                for (int n = 0; n < C::DN; ++n) asm volatile("" : "+a"(o[m][n]));
-                asm volatile("" : "+a"(lacc[m]));
                 const float mx = xmax(lmax[m]);
                 const float bmax = mx == -INFINITY ? -INFINITY : p.c * mx;  // (c = 0: every logit is 0)
                 const float mnew = bmax > mrun[m] + kSlack ? bmax : mrun[m];
@@ -449,13 +450,12 @@ struct Attn {
 #pragma unroll
                 for (int s = 0; s < C::KS; ++s)
                     qf[m][s] = __builtin_amdgcn_raw_buffer_load_b128(rq, (16 * m + i) * C::RB + (4 * s + g) * 16, 0, 0);
-            // The Q fragments are only ever MFMA operands, which may sit in the
-            // accumulator registers: keep them there, off the VGPRs the softmax and
-            // the register-staged fetch need.
+            // Take the fragments here (an empty use), so that the waits for these loads
+            // stay out of the key loop, where they would also wait for the ring's copies.
 #pragma unroll
             for (int m = 0; m < C::FM; ++m)
 #pragma unroll
-                for (int s = 0; s < C::KS; ++s) asm volatile("" : "+a"(qf[m][s]));
+                for (int s = 0; s < C::KS; ++s) asm volatile("" : "+v"(qf[m][s]));
         }
 
         Copy cp;

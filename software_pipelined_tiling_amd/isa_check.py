@@ -350,8 +350,9 @@ def check_attention(k: AttnKernel) -> Dict[str, bool]:
     most MFMAs): one block's MFMAs; DIRECT: its copies, one barrier and one vmcnt
     wait of (S-2) x copies, so the copies of the S-2 younger blocks stay in flight;
     REG: the block's global loads issued before the last MFMA and one vmcnt(0)
-    after it; SYNC: vmcnt(0) before the first MFMA; no scratch anywhere; the LDS
-    ring of S stages."""
+    after it; SYNC: vmcnt(0) before the first MFMA; no scratch anywhere; no
+    accumulator-register copies in the loop (the MFMAs write VGPRs, where the
+    softmax reads them); the LDS ring of S stages."""
     g = k.geometry
     body = steady_loop(k)
     L, S = g["loads_per_block"], k.stages
@@ -364,6 +365,7 @@ def check_attention(k: AttnKernel) -> Dict[str, bool]:
     bar = sum(x.startswith("s_barrier") for x in body)
     res = {"counts": _count_mfma(body) == g["mfma_per_block"],
            "clean": k.meta.get("scratch") == 0 and not any(x.startswith("scratch_") for x in body),
+           "vgpr_form": not any(x.startswith("v_accvgpr_") for x in body),
            "lds": k.meta.get("lds") == S * g["stage_bytes"]}
     if k.variant == "direct":
         res["copies"] = _count_copies(body) == L and bar == 1

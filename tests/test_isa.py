@@ -148,7 +148,8 @@ def test_attention_schedule(built_lib):
     """The attention consumer (both element types, head dimension 64 and 128, every
     producer): per key block the MFMAs of both products; DIRECT's copies, one barrier
     and one vmcnt((S-2) x copies) wait; REG's loads overlapped with MFMAs before their
-    vmcnt(0); SYNC's vmcnt(0) before any MFMA; no scratch; the LDS ring of S stages."""
+    vmcnt(0); SYNC's vmcnt(0) before any MFMA; no scratch; no accumulator-register
+    copies in the loop; the LDS ring of S stages."""
     ks = X.load_attention()
     assert sorted({(k.dtype, k.D, k.variant, k.stages) for k in ks}) == sorted(
         (dt, d, v, s) for dt in (0, 1) for d in (64, 128)
