@@ -490,9 +490,8 @@ struct Attn {
 #endif
                 dma_block(cp, dk, dv, lds0 + b * C::STAGE_BYTES, wave);
             }
-            uint32_t rs = 0;                                   // stage of block t
-            uint32_t ws = (C::S - 1) * C::STAGE_BYTES;         // stage of block t + S - 1
-            auto step = [&](int t, auto last) {
+            // rs: the stage of block t; ws: the stage of block t + S - 1 (that of t - 1)
+            auto step = [&](int t, auto last, auto rs, auto ws) {
                 wait_lgkmcnt0();                              // this wave's reads of block t-1 are done
                 wait_vmcnt<(C::S - 2) * C::LOADS>();          // its copies of block t have landed
                 barrier();                                    // block t visible; the stage of t-1 free
@@ -502,11 +501,24 @@ struct Attn {
 #endif
                 dma_block(cp, dk, dv, lds0 + ws, wave);       // block t+S-1 into that stage
                 block<decltype(last)::value>(p, smem + rs, L, qf, o, mrun, lacc, t, lane, [] {});
+            };
+            // Whole turns of the ring, unrolled, so that each block's stage is a constant
+            // (folded into the offsets of its LDS reads); none of them holds the last block.
+            int t = 0;
+            for (; t + C::S < nb; t += C::S)
+                static_for<0, C::S>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    step(t + j, std::false_type{}, std::integral_constant<uint32_t, j * C::STAGE_BYTES>{},
+                         std::integral_constant<uint32_t, (j + C::S - 1) % C::S * C::STAGE_BYTES>{});
+                });
+            // the rest (block t in stage 0), the last block with the mask
+            uint32_t rs = 0, ws = (C::S - 1) * C::STAGE_BYTES;
+            for (; t + 1 < nb; ++t) {
+                step(t, std::false_type{}, rs, ws);
                 rs = rs + C::STAGE_BYTES == (uint32_t)C::LDS_BYTES ? 0u : rs + C::STAGE_BYTES;
                 ws = ws + C::STAGE_BYTES == (uint32_t)C::LDS_BYTES ? 0u : ws + C::STAGE_BYTES;
-            };
-            for (int t = 0; t + 1 < nb; ++t) step(t, std::false_type{});  // the last block runs with the mask
-            if (nb > 0) step(nb - 1, std::true_type{});
+            }
+            if (nb > 0) step(nb - 1, std::true_type{}, rs, ws);
             wait_vmcnt<0>();  // no copy may still be writing this workgroup's LDS
         } else if constexpr (C::V == V_REG) {
             i32x4_t r[C::LOADS];
@@ -517,22 +529,32 @@ struct Attn {
                 wait_lgkmcnt0();
                 barrier();
             }
-            auto step = [&](int t, auto last) {
-                SPT_LDS char* cur = smem + (C::S == 2 ? (t & 1) : 0) * C::STAGE_BYTES;
-                SPT_LDS char* nxt = smem + (C::S == 2 ? ((t + 1) & 1) : 0) * C::STAGE_BYTES;
+            // cs: the stage of block t; ns: that of block t + 1
+            auto step = [&](int t, auto last, auto cs, auto ns) {
                 // block t+1 is fetched while block t is computed: issued once S = Q K^T is
                 // done (before it, the K fragments hold the registers the fetch needs),
                 // in flight over the softmax and O += P V (past the end: zero-length, zeros)
-                block<decltype(last)::value>(p, cur, L, qf, o, mrun, lacc, t, lane,
+                block<decltype(last)::value>(p, smem + cs, L, qf, o, mrun, lacc, t, lane,
                                              [&] { load_block(p, slice, t + 1, cp, r); });
                 if constexpr (C::S == 1) barrier();       // one buffer: every read of it done first
                 wait_vmcnt<0>();
-                store_block(nxt, wave, lane, r);
+                store_block(smem + ns, wave, lane, r);
                 wait_lgkmcnt0();
                 barrier();
             };
-            for (int t = 0; t + 1 < nb; ++t) step(t, std::false_type{});
-            if (nb > 0) step(nb - 1, std::true_type{});
+            // pairs of blocks, unrolled for S = 2 so that the stages are constants; none of
+            // them holds the last block
+            using Z = std::integral_constant<uint32_t, 0>;
+            using Z1 = std::integral_constant<uint32_t, (C::S - 1) * C::STAGE_BYTES>;
+            int t = 0;
+            if constexpr (C::S == 2)
+                for (; t + 2 < nb; t += 2) {
+                    step(t, std::false_type{}, Z{}, Z1{});
+                    step(t + 1, std::false_type{}, Z1{}, Z{});
+                }
+            // the rest (block t in stage 0), the last block with the mask
+            for (; t + 1 < nb; ++t) step(t, std::false_type{}, (t & 1) * Z1::value, ((t + 1) & 1) * Z1::value);
+            if (nb > 0) step(nb - 1, std::true_type{}, ((nb - 1) & 1) * Z1::value, (nb & 1) * Z1::value);
         } else {
             i32x4_t r[C::LOADS];
             auto step = [&](int t, auto last) {  // load -> barrier -> compute -> barrier

@@ -347,15 +347,18 @@ def load_attention(lib: Optional[str] = None) -> List[AttnKernel]:
 
 def check_attention(k: AttnKernel) -> Dict[str, bool]:
     """The key/value block loop of an attention kernel (the loop body holding the
-    most MFMAs): one block's MFMAs; DIRECT: its copies, one barrier and one vmcnt
-    wait of (S-2) x copies, so the copies of the S-2 younger blocks stay in flight;
-    REG: the block's global loads issued before the last MFMA and one vmcnt(0)
-    after it; SYNC: vmcnt(0) before the first MFMA; no scratch anywhere; no
-    accumulator-register copies in the loop (the MFMAs write VGPRs, where the
-    softmax reads them); the LDS ring of S stages."""
+    most MFMAs), which holds U blocks: one turn of the ring for DIRECT (U = S) and
+    for the two-stage REG (U = 2), unrolled so that each block's stage is a
+    constant, else one block.  Per block its MFMAs; DIRECT: its copies, one barrier
+    and one vmcnt wait of (S-2) x copies, so the copies of the S-2 younger blocks
+    stay in flight; REG: the block's global loads, each followed by MFMAs before
+    the vmcnt(0) that waits for it; SYNC: vmcnt(0) before the first MFMA; no
+    scratch anywhere; no accumulator-register copies in the loop (the MFMAs write
+    VGPRs, where the softmax reads them); the LDS ring of S stages."""
     g = k.geometry
     body = steady_loop(k)
     L, S = g["loads_per_block"], k.stages
+    U = S if k.variant == "direct" else 2 if (k.variant == "reg" and S == 2) else 1
     loads = [i for i, x in enumerate(body) if x.startswith("buffer_load") and not x.rstrip().endswith("lds")]
     if loads:  # read the loop as a cycle starting at its first global load
         body = body[loads[0]:] + body[:loads[0]]
@@ -363,18 +366,26 @@ def check_attention(k: AttnKernel) -> Dict[str, bool]:
     mf = [i for i, x in enumerate(body) if x.startswith("v_mfma")]
     vm = [(i, int(m.group(1))) for i, x in enumerate(body) for m in [re.search(r"vmcnt\((\d+)\)", x)] if m]
     bar = sum(x.startswith("s_barrier") for x in body)
-    res = {"counts": _count_mfma(body) == g["mfma_per_block"],
+    res = {"counts": _count_mfma(body) == U * g["mfma_per_block"],
            "clean": k.meta.get("scratch") == 0 and not any(x.startswith("scratch_") for x in body),
            "vgpr_form": not any(x.startswith("v_accvgpr_") for x in body),
            "lds": k.meta.get("lds") == S * g["stage_bytes"]}
     if k.variant == "direct":
-        res["copies"] = _count_copies(body) == L and bar == 1
-        res["vmcnt"] = [v for _, v in vm] == [(S - 2) * L]
+        res["copies"] = _count_copies(body) == U * L and bar == U
+        res["vmcnt"] = [v for _, v in vm] == [(S - 2) * L] * U
     elif k.variant == "reg":
-        # from the loads on: MFMAs before the first wait, which is vmcnt(0) (the compiler adds its
+        # after each load, MFMAs before the first wait, which is vmcnt(0) (the compiler adds its
         # own, already satisfied, partial waits before each staged ds_write)
-        res["copies"] = len(loads) == L and bar == (2 if S == 1 else 1)
-        res["vmcnt"] = bool(mf) and bool(vm) and vm[0][1] == 0 and mf[0] < vm[0][0]
+        res["copies"] = len(loads) == U * L and bar == U * (2 if S == 1 else 1)
+        ok = bool(vm)
+        for li in loads:
+            w = next((wi for wi, _ in vm if wi > li), None)
+            if w is None:
+                ok = False
+                break
+            last = max(x for x in loads if x < w)
+            ok = ok and dict(vm)[w] == 0 and any(last < m < w for m in mf)
+        res["vmcnt"] = ok
     else:
         # from the loads on: vmcnt(0) before any MFMA
         res["copies"] = len(loads) == L and bar == 2
