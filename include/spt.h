@@ -285,8 +285,9 @@ int spt_scale_by_two(int64_t n, const void* x, void* y, int stages, int blocks, 
  * the caller's to pass).  Errors: SPT_ERR_INVALID (negative size, Sk = 0 with
  * work to do -- a softmax over no keys --, null pointer, bad scale, enum
  * out of range, overlap), SPT_ERR_UNSUPPORTED (dtype, D, a variant/stage
- * pairing, sizes above 2^31-1, addresses outside the 48-bit range of buffer
- * descriptors), SPT_ERR_MISALIGNED, SPT_ERR_LAUNCH.  BH = 0 or Sq = 0 returns
+ * pairing, sizes above 2^31-1, one slice's K or V above 2^31 bytes
+ * (Sk * D * 2), addresses outside the 48-bit range of buffer descriptors),
+ * SPT_ERR_MISALIGNED, SPT_ERR_LAUNCH.  BH = 0 or Sq = 0 returns
  * SPT_OK without launching.  Asynchronous on `stream`, like spt_gemm.
  */
 int spt_attention(int64_t BH, int64_t Sq, int64_t Sk, int64_t D,

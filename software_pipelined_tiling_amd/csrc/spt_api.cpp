@@ -475,6 +475,10 @@ static int attention_impl(int64_t BH, int64_t Sq, int64_t Sk, int64_t D, const v
     if (Sq > INT32_MAX || Sk > INT32_MAX || BH > INT32_MAX) return fail(SPT_ERR_UNSUPPORTED, "size above 2^31-1");
     if ((uint64_t)BH * (uint64_t)Sq > (UINT64_C(1) << 40) || (uint64_t)BH * (uint64_t)Sk > (UINT64_C(1) << 40))
         return fail(SPT_ERR_UNSUPPORTED, "Q, K or V above 2^40 rows");
+    // (the kernel reads a slice's K and V through one buffer descriptor each, with
+    // 32-bit offsets that run up to two key blocks past the slice's end)
+    if ((uint64_t)Sk * (uint64_t)D * 2 > (UINT64_C(1) << 31))
+        return fail(SPT_ERR_UNSUPPORTED, "attention: one slice's K or V above 2^31 bytes");
     if (BH * ((Sq + 255) / 256) > INT32_MAX) return fail(SPT_ERR_UNSUPPORTED, "too many workgroups");
     if (!Q || !K || !V || !O) return fail(SPT_ERR_INVALID, "Q, K, V or O is null");
     if ((uintptr_t)Q % 16 || (uintptr_t)K % 16 || (uintptr_t)V % 16 || (uintptr_t)O % 16)

@@ -144,42 +144,36 @@ struct Attn {
                          __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
     }
 
-    // Key block t of this slice: the addresses of its first K and V rows and the bytes
-    // readable from them (up to the end of the slice, at most one block; zero past
-    // the last block).
-    static __device__ __forceinline__ void block_span(const AttnArgs& p, int slice, int t, const char*& kb,
-                                                      const char*& vb, uint32_t& ext)
+    // One descriptor per operand for the whole slice: its base lowered by BIAS, its
+    // extent the slice's bytes raised by as much.  Block t adds t x BKV rows to the
+    // register offsets, so the copies of the last block read zeros past Sk and those of
+    // blocks past the last read only zeros (the host keeps a slice within 2^31 bytes,
+    // so no offset wraps).  Nothing is recomputed per block but that offset.
+    static constexpr uint32_t BLK = (uint32_t)C::BKV * C::RB;  // bytes of one key block
+    static __device__ __forceinline__ void slice_desc(const AttnArgs& p, int slice, i32x4_t& dk, i32x4_t& dv)
     {
-        const long long row0 = (long long)slice * p.Sk + (long long)t * C::BKV;
-        const int rows = t < p.kv_blocks ? min(C::BKV, p.Sk - t * C::BKV) : 0;
-        ext = (uint32_t)(max(rows, 0) * C::RB);
-        kb = p.K + row0 * C::RB;
-        vb = p.V + row0 * C::RB;
-    }
-    // DIRECT descriptors of block t: bases lowered by BIAS (the register offsets are
-    // raised by as much), extents raised by it; zero extent past the last block.
-    static __device__ __forceinline__ void block_desc(const AttnArgs& p, int slice, int t, i32x4_t& dk, i32x4_t& dv)
-    {
-        const char *kb, *vb;
-        uint32_t ext;
-        block_span(p, slice, t, kb, vb, ext);
-        const uint32_t e = ext > 0 ? ext + BIAS : 0u;
-        dk = desc((uint64_t)(uintptr_t)kb - BIAS, e);
-        dv = desc((uint64_t)(uintptr_t)vb - BIAS, e);
+        const long long row0 = (long long)slice * p.Sk;
+        const uint32_t e = (uint32_t)p.Sk * C::RB + BIAS;
+        dk = desc((uint64_t)(uintptr_t)(p.K + row0 * C::RB) - BIAS, e);
+        dv = desc((uint64_t)(uintptr_t)(p.V + row0 * C::RB) - BIAS, e);
     }
 
     // DIRECT: the copies of one block into the stage at LDS byte address `st`.
-    static __device__ __forceinline__ void dma_block(const Copy& cp, i32x4_t dk, i32x4_t dv, uint32_t st, int wave)
+    // DIRECT: the copies of block t (descriptors of its slice) into the stage at LDS
+    // byte address `st`.
+    static __device__ __forceinline__ void dma_block(const Copy& cp, i32x4_t dk, i32x4_t dv, uint32_t st, int wave,
+                                                     int t)
     {
         const uint32_t mk = st + (uint32_t)(wave * C::CPW) * 1024u;
         const uint32_t mv = mk + (uint32_t)C::KV_BYTES;
+        const uint32_t bo = (uint32_t)t * BLK + BIAS;
         static_for<0, C::CPW>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
-            dma16<j * 1024, j == 0>(dk, mk, cp.goff[j] - j * 1024 + BIAS);
+            dma16<j * 1024, j == 0>(dk, mk, (int)((uint32_t)cp.goff[j] - j * 1024u + bo));
         });
         static_for<0, C::CPW>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
-            dma16<j * 1024, j == 0>(dv, mv, cp.goff[C::CPW + j] - j * 1024 + BIAS);
+            dma16<j * 1024, j == 0>(dv, mv, (int)((uint32_t)cp.goff[C::CPW + j] - j * 1024u + bo));
         });
     }
 
@@ -202,19 +196,23 @@ struct Attn {
     }
 #endif
 
-    // REG / SYNC: the same chunks through VGPRs.
-    static __device__ __forceinline__ void load_block(const AttnArgs& p, int slice, int t, const Copy& cp,
-                                                      i32x4_t (&r)[C::LOADS])
+    // REG / SYNC: the same chunks through VGPRs, from one descriptor per operand for
+    // the slice (reads past Sk return zeros).
+    static __device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const char* base, const AttnArgs& p,
+                                                                        int slice)
     {
-        const char *kb, *vb;
-        uint32_t ext;
-        block_span(p, slice, t, kb, vb, ext);
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, ext), rv = make_rsrc(vb, ext);
-#pragma unroll
-        for (int j = 0; j < C::CPW; ++j) r[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, cp.goff[j], 0, 0);
+        return make_rsrc(base + (long long)slice * p.Sk * C::RB, (uint32_t)p.Sk * C::RB);
+    }
+    static __device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int t,
+                                                      const Copy& cp, i32x4_t (&r)[C::LOADS])
+    {
+        const uint32_t bo = (uint32_t)t * BLK;
 #pragma unroll
         for (int j = 0; j < C::CPW; ++j)
-            r[C::CPW + j] = __builtin_amdgcn_raw_buffer_load_b128(rv, cp.goff[C::CPW + j], 0, 0);
+            r[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)((uint32_t)cp.goff[j] + bo), 0, 0);
+#pragma unroll
+        for (int j = 0; j < C::CPW; ++j)
+            r[C::CPW + j] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)((uint32_t)cp.goff[C::CPW + j] + bo), 0, 0);
     }
     static __device__ __forceinline__ void store_block(SPT_LDS char* st, int wave, int lane,
                                                        const i32x4_t (&r)[C::LOADS])
@@ -481,25 +479,24 @@ struct Attn {
         const int nb = p.kv_blocks;
         if constexpr (C::V == V_DIRECT) {
             i32x4_t dk, dv;
+            slice_desc(p, slice, dk, dv);
             // prologue: blocks 0 .. S-2 into stages 0 .. S-2
 #pragma unroll
             for (int b = 0; b < C::S - 1; ++b) {
-                block_desc(p, slice, b, dk, dv);
 #ifdef SPT_POISON
                 poison(lds0 + b * C::STAGE_BYTES, wave, lane);
 #endif
-                dma_block(cp, dk, dv, lds0 + b * C::STAGE_BYTES, wave);
+                dma_block(cp, dk, dv, lds0 + b * C::STAGE_BYTES, wave, b);
             }
             // rs: the stage of block t; ws: the stage of block t + S - 1 (that of t - 1)
             auto step = [&](int t, auto last, auto rs, auto ws) {
                 wait_lgkmcnt0();                              // this wave's reads of block t-1 are done
                 wait_vmcnt<(C::S - 2) * C::LOADS>();          // its copies of block t have landed
                 barrier();                                    // block t visible; the stage of t-1 free
-                block_desc(p, slice, t + C::S - 1, dk, dv);
 #ifdef SPT_POISON
                 poison(lds0 + ws, wave, lane);
 #endif
-                dma_block(cp, dk, dv, lds0 + ws, wave);       // block t+S-1 into that stage
+                dma_block(cp, dk, dv, lds0 + ws, wave, t + C::S - 1);  // block t+S-1 into that stage
                 block<decltype(last)::value>(p, smem + rs, L, qf, o, mrun, lacc, t, lane, [] {});
             };
             // Whole turns of the ring, unrolled, so that each block's stage is a constant
@@ -521,9 +518,10 @@ struct Attn {
             if (nb > 0) step(nb - 1, std::true_type{}, rs, ws);
             wait_vmcnt<0>();  // no copy may still be writing this workgroup's LDS
         } else if constexpr (C::V == V_REG) {
+            const __amdgpu_buffer_rsrc_t rk = slice_rsrc(p.K, p, slice), rv = slice_rsrc(p.V, p, slice);
             i32x4_t r[C::LOADS];
             if (nb > 0) {  // prologue: block 0 into stage 0
-                load_block(p, slice, 0, cp, r);
+                load_block(rk, rv, 0, cp, r);
                 wait_vmcnt<0>();
                 store_block(smem, wave, lane, r);
                 wait_lgkmcnt0();
@@ -535,7 +533,7 @@ struct Attn {
                 // done (before it, the K fragments hold the registers the fetch needs),
                 // in flight over the softmax and O += P V (past the end: zero-length, zeros)
                 block<decltype(last)::value>(p, smem + cs, L, qf, o, mrun, lacc, t, lane,
-                                             [&] { load_block(p, slice, t + 1, cp, r); });
+                                             [&] { load_block(rk, rv, t + 1, cp, r); });
                 if constexpr (C::S == 1) barrier();       // one buffer: every read of it done first
                 wait_vmcnt<0>();
                 store_block(smem + ns, wave, lane, r);
@@ -556,9 +554,10 @@ struct Attn {
             for (; t + 1 < nb; ++t) step(t, std::false_type{}, (t & 1) * Z1::value, ((t + 1) & 1) * Z1::value);
             if (nb > 0) step(nb - 1, std::true_type{}, ((nb - 1) & 1) * Z1::value, (nb & 1) * Z1::value);
         } else {
+            const __amdgpu_buffer_rsrc_t rk = slice_rsrc(p.K, p, slice), rv = slice_rsrc(p.V, p, slice);
             i32x4_t r[C::LOADS];
             auto step = [&](int t, auto last) {  // load -> barrier -> compute -> barrier
-                load_block(p, slice, t, cp, r);
+                load_block(rk, rv, t, cp, r);
                 wait_vmcnt<0>();
                 store_block(smem, wave, lane, r);
                 wait_lgkmcnt0();

@@ -59,7 +59,7 @@ import struct
 import subprocess
 import sys
 import tempfile
-from typing import Dict, List, Optional
+from typing import Tuple, Dict, List, Optional
 
 LLVM = os.environ.get("ROCM_LLVM_BIN", "/opt/rocm/llvm/bin")
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -405,12 +405,12 @@ def _count_copies(body: List[str]) -> int:
     return sum(x.startswith("buffer_load") and x.rstrip().endswith("lds") for x in body)
 
 
-def loop_regions(k) -> List[List[str]]:
-    """Instructions from the target of every backward branch to the branch
-    (the body of a loop, as laid out)."""
+def loop_spans(k) -> List[Tuple[int, int]]:
+    """(first, last) indices into k.instrs of every loop body: from the target of a
+    backward branch to the branch, as laid out."""
     addr = [int(i.split("|")[0], 16) for i in k.instrs]
     pos = {a: n for n, a in enumerate(addr)}
-    out: List[List[str]] = []
+    out: List[Tuple[int, int]] = []
     for j, ins in enumerate(k.instrs):
         m2 = re.match(r"s_c?branch\w*\s+(\d+)$", _op(ins))
         if not m2:
@@ -420,8 +420,25 @@ def loop_regions(k) -> List[List[str]]:
         nxt = addr[j + 1] if j + 1 < len(addr) else addr[j] + 4
         tgt = nxt + 4 * simm
         if tgt <= addr[j] and tgt in pos:
-            out.append([_op(x) for x in k.instrs[pos[tgt]:j + 1]])
+            out.append((pos[tgt], j))
     return out
+
+
+def loop_regions(k) -> List[List[str]]:
+    """Instructions from the target of every backward branch to the branch
+    (the body of a loop, as laid out)."""
+    return [[_op(x) for x in k.instrs[a:b + 1]] for a, b in loop_spans(k)]
+
+
+def steady_span(k, key=None) -> Tuple[int, int]:
+    """(first, last) indices into k.instrs of the loop that steady_loop returns."""
+    key = key or _count_mfma
+    best, bs = None, []
+    for a, b in loop_spans(k):
+        body = [_op(x) for x in k.instrs[a:b + 1]]
+        if best is None or key(body) > key(bs) or (key(body) == key(bs) > 0 and len(body) < len(bs)):
+            best, bs = (a, b), body
+    return best
 
 
 def steady_loop(k, key=_count_mfma) -> List[str]:

@@ -281,6 +281,32 @@ def test_panel_above_2gib_is_refused(L):
     assert "2 GiB" in spt.spt_last_error()
 
 
+QA, KA, VA, OA = 0x1000000, 0x2000000, 0x3000000, 0x4000000  # fake, aligned, far apart
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(BH=-1), spt.SPT_ERR_INVALID), (dict(Sk=0), spt.SPT_ERR_INVALID), (dict(scale=-1.0), spt.SPT_ERR_INVALID),
+    (dict(variant=4), spt.SPT_ERR_INVALID), (dict(stages=5), spt.SPT_ERR_INVALID),
+    (dict(D=96), spt.SPT_ERR_UNSUPPORTED), (dict(dtype=spt.I8), spt.SPT_ERR_UNSUPPORTED),
+    (dict(variant=spt.VARIANT_SYNC, stages=2), spt.SPT_ERR_UNSUPPORTED),
+    (dict(variant=spt.VARIANT_DIRECT, stages=1), spt.SPT_ERR_UNSUPPORTED),
+    (dict(Q=0), spt.SPT_ERR_INVALID), (dict(O=KA + 64), spt.SPT_ERR_INVALID),   # null, O overlaps K
+    (dict(K=KA + 8), spt.SPT_ERR_MISALIGNED),
+    # one slice's K of 2^31 + 256 bytes (the kernel's 32-bit buffer offsets): refused
+    (dict(BH=1, Sk=(1 << 23) + 1, D=128), spt.SPT_ERR_UNSUPPORTED),
+    (dict(BH=1, Sk=(1 << 24) + 1, D=64), spt.SPT_ERR_UNSUPPORTED),
+])
+def test_attention_validation(L, kw, status):
+    """spt_attention refuses bad arguments before any device call (fake pointers)."""
+    a = dict(BH=2, Sq=64, Sk=64, D=64, Q=QA, K=KA, V=VA, O=OA, scale=0.125, dtype=spt.F16, variant=0, stages=0)
+    a.update(kw)
+    assert spt.spt_attention(a["BH"], a["Sq"], a["Sk"], a["D"], a["Q"], a["K"], a["V"], a["O"], a["scale"],
+                             a["dtype"], 0, a["variant"], a["stages"]) == status
+    assert spt.spt_last_error() != ""
+    if kw.get("Sk", 0) > (1 << 22):
+        assert "2^31 bytes" in spt.spt_last_error()
+
+
 def test_last_error_describes_the_most_recent_call():
     """spt_last_error() holds a message after a refused call and is empty after any
     call that returned SPT_OK, including calls with nothing to launch."""

@@ -234,7 +234,7 @@ def test_attention_checks_catch_planted_faults(built_lib):
         k = ks[(0, 128, "direct", st)]
         assert all(X.check_attention(k).values())
         ops = _ops(k)
-        body_start = ops.index(X.steady_loop(k)[0])
+        body_start = X.steady_span(k)[0]
         vm = next(i for i in range(body_start, len(ops)) if re.search(r"vmcnt\(\d+\)", ops[i]))
         want = int(re.search(r"vmcnt\((\d+)\)", ops[vm]).group(1))
         dma = next(i for i in range(vm, len(ops)) if _is_dma(ops[i]))
@@ -249,9 +249,8 @@ def test_attention_checks_catch_planted_faults(built_lib):
         k = ks[(0, 128, v, st)]
         assert all(X.check_attention(k).values())
         ops = _ops(k)
-        loop = X.steady_loop(k)
-        start = ops.index(loop[0])
-        idx = range(start, start + len(loop))
+        start, end = X.steady_span(k)
+        idx = range(start, end + 1)
         first_load = next(i for i in idx if ops[i].startswith("buffer_load"))
         wait = next(i for i in idx if i > first_load and re.search(r"vmcnt\(0\)", ops[i]))
         mfma_after = next(i for i in idx if i > first_load and ops[i].startswith("v_mfma"))
