@@ -114,6 +114,10 @@ struct Attn {
     // How far (in the base-2 logit domain) a row's maximum may exceed the reference
     // before the reference moves: probabilities stay below 2^8, well inside fp16.
     static constexpr float kSlack = 8.0f;
+    // A row's reference m and the bound m + kSlack its scaled maximum is tested against.
+    struct RowRef {
+        float m, thr;
+    };
 
     static __device__ __forceinline__ constexpr int swz_k(int r) { return (r / C::RPL) & (C::NCH - 1); }
     static __device__ __forceinline__ constexpr int swz_v(int r) { return ((r / C::RPL) & (C::NCH / 2 - 1)) << 1; }
@@ -309,7 +313,7 @@ struct Attn {
     template <bool MASK, class F>
     static __device__ __forceinline__ void block(const AttnArgs& p, const SPT_LDS char* st, const Lanes& L,
                                                  const i32x4_t (&qf)[C::FM][C::KS], acc_t (&o)[C::FM][C::DN],
-                                                 float (&mrun)[C::FM], acc_t (&lacc)[C::FM], int t, int lane, F&& mid)
+                                                 RowRef (&ref)[C::FM], acc_t (&lacc)[C::FM], int t, int lane, F&& mid)
     {
         constexpr int NK = C::KS * C::NB;  // K fragment f: d-step f / NB, key block f % NB
         constexpr int NF = C::US * C::DN;  // V fragment f: key-step f / DN, column block f % DN
@@ -347,11 +351,12 @@ struct Attn {
 #pragma unroll
                 for (int e = E / 2; e < E; ++e) mx = fmaxf(mx, valid(e) ? sc(e) : -INFINITY);
                 lmax[m] = mx;
-                up[m] = mx != -INFINITY && p.c * mx > mrun[m] + kSlack;
+                // (a row with no valid key has mx = -inf, and c mx is -inf or NaN: never above)
+                up[m] = p.c * mx > ref[m].thr;
             } else if constexpr (j <= 5) {
 #pragma unroll
                 for (int e = (j - 2) * E / 4; e < (j - 1) * E / 4; ++e) {
-                    const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(sc(e), p.c, -mrun[m]));
+                    const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(sc(e), p.c, -ref[m].m));
                     pe[m][e] = valid(e) ? v : 0.f;
                     // (an empty use, so that the compiler does not sink this work past the
                     // ballot's branch, out of the MFMA group it is meant to overlap)
@@ -370,9 +375,9 @@ struct Attn {
             if (__builtin_expect(__builtin_amdgcn_ballot_w64(up[m]) != 0, 0)) {
                 const float mx = xmax(lmax[m]);
                 const float bmax = mx == -INFINITY ? -INFINITY : p.c * mx;  // (c = 0: every logit is 0)
-                const float mnew = bmax > mrun[m] + kSlack ? bmax : mrun[m];
-                const float alpha = __builtin_amdgcn_exp2f(mrun[m] - mnew);  // 0 in the first block
-                mrun[m] = mnew;
+                const float mnew = bmax > ref[m].thr ? bmax : ref[m].m;
+                const float alpha = __builtin_amdgcn_exp2f(ref[m].m - mnew);  // 0 in the first block
+                ref[m] = RowRef{mnew, mnew + kSlack};
                 lacc[m] *= alpha;
 #pragma unroll
                 for (int n = 0; n < C::DN; ++n) o[m][n] *= alpha;
@@ -466,11 +471,11 @@ struct Attn {
         setup_lanes(lane, L);
 
         acc_t o[C::FM][C::DN];
-        float mrun[C::FM];
+        RowRef ref[C::FM];
         acc_t lacc[C::FM];  // row sums of the probabilities: every element of lane (g, i) holds row i's
 #pragma unroll
         for (int m = 0; m < C::FM; ++m) {
-            mrun[m] = -INFINITY;
+            ref[m] = RowRef{-INFINITY, -INFINITY};
             lacc[m] = (acc_t){0, 0, 0, 0};
 #pragma unroll
             for (int n = 0; n < C::DN; ++n) o[m][n] = (acc_t){0, 0, 0, 0};
@@ -497,7 +502,7 @@ struct Attn {
                 poison(lds0 + ws, wave, lane);
 #endif
                 dma_block(cp, dk, dv, lds0 + ws, wave, t + C::S - 1);  // block t+S-1 into that stage
-                block<decltype(last)::value>(p, smem + rs, L, qf, o, mrun, lacc, t, lane, [] {});
+                block<decltype(last)::value>(p, smem + rs, L, qf, o, ref, lacc, t, lane, [] {});
             };
             // Whole turns of the ring, unrolled, so that each block's stage is a constant
             // (folded into the offsets of its LDS reads); none of them holds the last block.
@@ -532,7 +537,7 @@ struct Attn {
                 // block t+1 is fetched while block t is computed: issued once S = Q K^T is
                 // done (before it, the K fragments hold the registers the fetch needs),
                 // in flight over the softmax and O += P V (past the end: zero-length, zeros)
-                block<decltype(last)::value>(p, smem + cs, L, qf, o, mrun, lacc, t, lane,
+                block<decltype(last)::value>(p, smem + cs, L, qf, o, ref, lacc, t, lane,
                                              [&] { load_block(rk, rv, t + 1, cp, r); });
                 if constexpr (C::S == 1) barrier();       // one buffer: every read of it done first
                 wait_vmcnt<0>();
@@ -562,7 +567,7 @@ struct Attn {
                 store_block(smem, wave, lane, r);
                 wait_lgkmcnt0();
                 barrier();
-                block<decltype(last)::value>(p, smem, L, qf, o, mrun, lacc, t, lane, [] {});
+                block<decltype(last)::value>(p, smem, L, qf, o, ref, lacc, t, lane, [] {});
                 barrier();
             };
             for (int t = 0; t + 1 < nb; ++t) step(t, std::false_type{});
