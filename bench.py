@@ -318,8 +318,9 @@ def attention_bench():
                     "asynchronous copies are faster); the pages measured 0.95 for flash attention on GA104",
             "pipelined_over_sync": round(res["sync1"]["us"] / min(best_d, best_r), 3)}
     # the compute/load ratio per key block (spt_attention.hip: 256 query rows, 32 keys of
-    # 128 columns per block, 4 waves): 64 MFMAs per wave per 4 copies per thread
-    res["ratio"] = {"mfma_per_copy": 16.0, "flop_per_byte": 256.0,
+    # 128 columns per block, 8 waves): 34 MFMAs per wave (32 of the two products, 2 row
+    # sums) per 2 copies per thread
+    res["ratio"] = {"mfma_per_copy": 17.0, "flop_per_byte": 256.0,
                     "gemm_headline_tile": {"mfma_per_copy": 8.0, "flop_per_byte": 128.0}}
     return res
 

@@ -273,10 +273,10 @@ int spt_scale_by_two(int64_t n, const void* x, void* y, int stages, int blocks, 
  * slower) and counts its work as 4 * BH * Sq * Sk * D FLOP (Schritt 1).
  * Key/value blocks stream through the producer `variant` (SPT_VARIANT_SYNC
  * with 1 stage, SPT_VARIANT_REG with 1-2, SPT_VARIANT_DIRECT with 2-3;
- * SPT_VARIANT_AUTO / stages 0 = the library's choice), the online softmax
- * runs in fp32, and the probabilities are rounded to the input type for the
- * second product; each row is divided by the sum of those rounded
- * probabilities.
+ * SPT_VARIANT_AUTO picks DIRECT; stages 0 picks two for REG and DIRECT),
+ * the online softmax runs in fp32, and the probabilities are rounded to the
+ * input type for the second product; each row is divided by the sum of
+ * those rounded probabilities.
  *
  * dtype SPT_F16 or SPT_BF16 for Q, K, V; O is fp32.  D (head dimension) is 64
  * or 128.  Layouts (contiguous, DEVICE pointers owned by the caller, 16-byte

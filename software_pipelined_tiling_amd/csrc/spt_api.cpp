@@ -463,9 +463,10 @@ static int attention_impl(int64_t BH, int64_t Sq, int64_t Sk, int64_t D, const v
     if (stages < 0 || stages > 4) return fail(SPT_ERR_INVALID, "stages %d not in 0..4", stages);
     if (BH < 0 || Sq < 0 || Sk < 0 || D < 0) return fail(SPT_ERR_INVALID, "negative size");
     if (!(scale >= 0.0f) || scale > 3.0e38f) return fail(SPT_ERR_INVALID, "scale must be finite and >= 0");
-    // AUTO: the DIRECT ring of three stages (measured the fastest producer at 4096 keys)
+    // AUTO: the DIRECT ring of two stages (measured the fastest producer at 4096 keys;
+    // three stages ran 0-3% slower and take more registers)
     if (variant == V_AUTO) variant = V_DIRECT;
-    if (stages == 0) stages = variant == V_SYNC ? 1 : variant == V_REG ? 2 : 3;
+    if (stages == 0) stages = variant == V_SYNC ? 1 : 2;
     if (!((variant == V_SYNC && stages == 1) || (variant == V_REG && (stages == 1 || stages == 2)) ||
           (variant == V_DIRECT && (stages == 2 || stages == 3))))
         return fail(SPT_ERR_UNSUPPORTED, "attention: variant %d has no %d-stage form", variant, stages);
