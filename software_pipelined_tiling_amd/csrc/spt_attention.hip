@@ -51,9 +51,14 @@
 // XOR-ed by (r' mod pairs).  The producer computes which global chunk belongs
 // at each position; a copy of one wave moves 1 KiB of whole rows.
 //
-// Edges.  Keys past Sk: the last block's descriptor ends at the slice, so its
-// copies read zeros there, and those keys get no maximum and weight 0.
-// Query rows past Sq read zeros and are never stored.
+// Edges.  Keys past Sk: K and V are read through one descriptor per slice,
+// which ends at the slice, so the last block's copies read zeros there, and
+// those keys get no maximum and weight 0.  Query rows past Sq read zeros and
+// are never stored.
+//
+// Loops.  The DIRECT loop is unrolled by one turn of the ring (the two-stage
+// REG loop by two blocks), so that each block's LDS stage is a constant folded
+// into the immediate offsets of its fragment reads.
 //
 // Registers.  This unit is built with every MFMA in its VGPR form (the build
 // passes -amdgpu-mfma-vgpr-form to the compiler): the softmax reads the scores
