@@ -163,7 +163,8 @@ def test_torch_wrapper(oracle_mod):
     parity.check_attention(O.cpu().numpy(), oracle_mod.attention(Q, K, V, "bf16", 1 / np.sqrt(128)), V, "bf16")
 
 
-@pytest.mark.parametrize("variant,stages", [("auto", 0), ("direct", 2), ("reg", 1), ("reg", 2), ("sync", 1)])
+@pytest.mark.parametrize("variant,stages", [("auto", 0), ("direct", 2), ("direct", 3), ("reg", 1), ("reg", 2),
+                                            ("sync", 1)])
 def test_full_size_workload(oracle_mod, variant, stages):
     """The benchmark's workload (32 slices x 4096 x 4096 x 128, fp16) in every
     configuration bench.py times, against the oracle over all of O."""
@@ -175,3 +176,26 @@ def test_full_size_workload(oracle_mod, variant, stages):
     Q, K, V, ref = test_full_size_workload.ref
     O = run(Q, K, V, "f16", 1 / np.sqrt(w.D), variant, stages)
     parity.check_attention(O, ref, V, "f16")
+
+
+def test_full_size_bf16_d64_sampled_rows(oracle_mod):
+    """bf16 at head dimension 64: 64 slices x 4096 queries x 4096 keys (the benchmark
+    workload's FLOP, 64 key blocks per slice) under every producer, bit-identical to each
+    other over all of O, and against the oracle on 48 query rows of every slice spread
+    over all 16 query blocks (attention is row-wise: those rows of O are the attention
+    of those rows of Q alone)."""
+    w = I.AttentionWorkload("bf16 attention 64 x 4096 x 4096 x 64", 75, 64, 4096, 4096, 64, "bf16")
+    Q, K, V = I.make_qkv(w)
+    scale = 1 / np.sqrt(w.D)
+    rows = np.unique(np.concatenate([np.arange(0, w.Sq, 256) + o for o in (0, 127, 255)]))
+    print("[gpu] oracle attention bf16 d64, sampled rows", flush=True)
+    ref = oracle_mod.attention(np.ascontiguousarray(Q[:, rows]), K, V, "bf16", scale)
+    first = None
+    for variant, stages in VARIANTS:
+        O = run(Q, K, V, "bf16", scale, variant, stages)
+        parity.check_attention(np.ascontiguousarray(O[:, rows]), ref, V, "bf16")
+        if first is None:
+            first = O
+        else:
+            assert np.array_equal(O.view(np.uint32), first.view(np.uint32)), (variant, stages)
+
