@@ -1,11 +1,12 @@
-"""Concurrent calls and captured launches of the GEMM, on an MI355X.
+"""Concurrent calls and captured launches of the GEMM and the attention
+consumer, on an MI355X.
 
 Between calls the library keeps only a thread-local error message, so calls
-from several host threads, each on its own stream, must each give the C of a
-single call.  A call is one kernel launch (two where a last, nearly empty
-round runs as a second grid) with no allocation, copy or memset, so it can
-also be captured into a HIP graph: every replay must give the C of
-an eager call on the operands the buffers hold at that moment.
+from several host threads, each on its own stream, must each give the output
+of a single call.  A call is one kernel launch (two where a GEMM's last,
+nearly empty round runs as a second grid) with no allocation, copy or memset,
+so it can also be captured into a HIP graph: every replay must give the
+output of an eager call on the inputs the buffers hold at that moment.
 """
 from __future__ import annotations
 
@@ -120,3 +121,80 @@ def test_captured_in_a_hip_graph(oracle_mod, dtype, b_col, M, N, K):
         torch.cuda.synchronize()
         got = C.cpu().numpy()
         assert np.array_equal(got.view(np.uint32), eager[i % 2].view(np.uint32)), f"replay {i}"
+
+
+def _attention_inputs(seed, dtype="f16", BH=3, Sq=300, Sk=333, D=128):
+    from software_pipelined_tiling_amd import inputs as I
+    from tests.test_attention_gpu import dev
+    Q, K, V = I.make_qkv(I.AttentionWorkload("t", seed, BH, Sq, Sk, D, dtype))
+    return (Q, K, V), tuple(dev(x, dtype) for x in (Q, K, V))
+
+
+@pytest.mark.parametrize("variant,stages", [("direct", 2), ("reg", 2)])
+def test_attention_captured_in_a_hip_graph(oracle_mod, variant, stages):
+    """One attention call captured into a graph, replayed six times over two input
+    sets that eager copies swap in between replays (O reset to NaN each time):
+    every replay bit-identical to the eager call on the same inputs, which matches
+    the oracle."""
+    sets = [_attention_inputs(81 + i) for i in range(2)]
+    eager = []
+    for (Q, K, V), (dQ, dK, dV) in sets:
+        O = spt.attention(dQ, dK, dV, variant=variant, stages=stages)
+        torch.cuda.synchronize()
+        eager.append(O.cpu().numpy())
+        parity.check_attention(eager[-1], oracle_mod.attention(Q, K, V, "f16", 1 / np.sqrt(128)), V, "f16")
+    dQ, dK, dV = (x.clone() for x in sets[0][1])
+    O = torch.full(dQ.shape, float("nan"), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # a first call outside the capture
+        spt.attention(dQ, dK, dV, out=O, variant=variant, stages=stages)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    print(f"[gpu] capture attention {variant}/{stages}", flush=True)
+    with torch.cuda.graph(g):
+        spt.attention(dQ, dK, dV, out=O, variant=variant, stages=stages)
+    torch.cuda.synchronize()
+    sentinel = torch.full_like(O, float("nan"))
+    for i in range(6):
+        src = sets[i % 2][1]
+        for d, s in zip((dQ, dK, dV), src):
+            d.copy_(s)
+        O.copy_(sentinel)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(O.cpu().numpy().view(np.uint32), eager[i % 2].view(np.uint32)), f"replay {i}"
+
+
+def test_attention_threads_on_their_own_streams():
+    """Four host threads, four attention calls each, on four streams into four
+    outputs: every output bit-identical to one eager call's."""
+    _, (dQ, dK, dV) = _attention_inputs(85, "bf16", BH=2, Sq=513, Sk=1000, D=64)
+    expect = spt.attention(dQ, dK, dV)
+    torch.cuda.synchronize()
+    expect = expect.cpu().numpy()
+    nthreads, reps = 4, 4
+    outs = [torch.full(dQ.shape, float("nan"), dtype=torch.float32, device="cuda") for _ in range(nthreads)]
+    streams = [torch.cuda.Stream() for _ in range(nthreads)]
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(i):
+        for r in range(reps):
+            try:
+                spt.attention(dQ, dK, dV, out=outs[i], stream=streams[i].cuda_stream)
+            except Exception as e:  # noqa: BLE001 -- reported below
+                errors.append((i, r, repr(e)))
+
+    print(f"[gpu] {nthreads} threads x {reps} attention calls", flush=True)
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(nthreads)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for o in outs:
+        assert np.array_equal(o.cpu().numpy().view(np.uint32), expect.view(np.uint32))
