@@ -252,8 +252,9 @@ int spt_plan(int dtype, int64_t M, int64_t N, int64_t K,
  * elements are staged global -> LDS through a ring of `stages` stages (1 =
  * the synchronous loop, 2..4 = asynchronous copies; 0 = 3, the page's
  * choice); each of `blocks` workgroups of 256 threads walks its own stream of
- * tiles (0 = the library's choice: 512 for 3-4 stages, 1024 for 1-2, never
- * more than there are tiles; 1 = the page's single-block demonstration).
+ * tiles (0 = the library's choice: 1024 / 768 / 512 / 256 for 1 / 2 / 3 / 4
+ * stages, never more than there are tiles; 1 = the page's single-block
+ * demonstration).
  * Every result is exact (doubling is exact in float).  n = 0 returns SPT_OK
  * without launching; n < 0, stages outside 0..4 or blocks < 0 give
  * SPT_ERR_INVALID; n > 2^40 gives SPT_ERR_UNSUPPORTED.  Asynchronous on

@@ -443,11 +443,13 @@ static int scale_by_two_impl(int64_t n, const void* x, void* y, int stages, int 
     if (xa >> 47 || ya >> 47 || xa < 65536 || ya < 65536)
         return fail(SPT_ERR_UNSUPPORTED, "x or y outside the device address range of buffer descriptors");
     const int64_t tiles = (n + 1023) / 1024;
-    // default: the pages' three stages.  Blocks (measured on MI355X at 2^28
-    // floats): a ring of 3-4 stages keeps enough copies in flight with two
-    // blocks per CU; S <= 2 needs about four to hide the same latency.
+    // default: the pages' three stages.  Blocks: about 3-4 MiB of copies in
+    // flight over the chip, blocks x (S - 1) x 4 KiB (measured on MI355X at 2^28
+    // floats, TB/s: S = 2 with 512 / 768 / 1024 blocks 4.97 / 5.74 / 5.61; S = 3
+    // with 256 / 512 / 768 5.08 / 5.79 / 5.59; S = 4 with 256 / 512 5.94 / 5.34;
+    // more in flight runs slower still, 4.3-4.6 at 2048-4096 blocks).
     const int s = stages == 0 ? 3 : stages;
-    const int64_t want = blocks != 0 ? blocks : (s >= 3 ? 512 : 1024);
+    const int64_t want = blocks != 0 ? blocks : (s == 1 ? 1024 : s == 2 ? 768 : s == 3 ? 512 : 256);
     const int64_t g = want < tiles ? want : tiles;
     const hipError_t err = launch_scale_by_two(x, y, n, s, (unsigned)g, (hipStream_t)stream);
     if (err != hipSuccess) return fail(SPT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(err));
